@@ -1,0 +1,200 @@
+"""Seeded synthetic inputs for the five attention workloads.
+
+This module holds no attention arithmetic: it only draws random tensors and
+lays them out (dense BHTD tensors, a page pool and its block table).  The GPU
+tests, the oracle checks and the benchmark all take their inputs from here, so
+both sides of every comparison see exactly the same values.
+
+Draws use a CPU ``torch.Generator`` seeded per workload: values are iid
+N(0, 1) in float32, drawn in the order Q, K, V, then rounded to the target
+dtype (round to nearest even for bfloat16).  Paged inputs draw seq_lens
+first, then the page permutation, then q, then the K and V pools.
+"""
+
+from dataclasses import dataclass
+import math
+
+import torch
+
+PAGE_SIZE = 16
+
+
+@dataclass(frozen=True)
+class PrefillShape:
+    B: int
+    Hq: int
+    Hkv: int
+    T: int
+    d: int
+    dtype: torch.dtype
+
+    def flops(self) -> int:
+        """Algorithmic flops: QK^T and PV over the causal triangle, diagonal included."""
+        return 2 * self.B * self.Hq * self.d * self.T * (self.T + 1)
+
+
+@dataclass(frozen=True)
+class DecodeShape:
+    B: int
+    Hq: int
+    Hkv: int
+    d: int
+    page_size: int
+    L_lo: int
+    L_hi: int
+    dtype: torch.dtype
+
+    @property
+    def max_pages_per_seq(self) -> int:
+        return -(-self.L_hi // self.page_size)
+
+
+# The five workloads.  Prefill inputs are drawn with seed = workload number,
+# decode inputs with seed = 100 + workload number.
+WORKLOADS = {
+    1: {"prefill": PrefillShape(1, 4, 4, 128, 64, torch.float32)},
+    2: {"prefill": PrefillShape(1, 16, 8, 512, 128, torch.bfloat16)},
+    3: {"prefill": PrefillShape(2, 32, 8, 2048, 128, torch.bfloat16)},
+    4: {"decode": DecodeShape(32, 16, 8, 128, PAGE_SIZE, 32, 2048, torch.bfloat16)},
+    5: {
+        "prefill": PrefillShape(1, 32, 8, 8192, 128, torch.bfloat16),
+        "decode": DecodeShape(64, 32, 8, 128, PAGE_SIZE, 1024, 8192, torch.bfloat16),
+    },
+}
+
+WORKLOAD_NAMES = {
+    1: "causal MHA prefill fp32 B1 H4 T128 d64",
+    2: "causal GQA prefill bf16 B1 Hq16 Hkv8 T512 d128",
+    3: "causal GQA prefill bf16 B2 Hq32 Hkv8 T2048 d128",
+    4: "paged decode bf16 B32 Hq16 Hkv8 d128 page16 L~U[32,2048]",
+    5: "mixed: prefill bf16 B1 Hq32 Hkv8 T8192 d128 + paged decode bf16 B64 Hq32 Hkv8 d128 page16 L~U[1024,8192]",
+}
+
+
+def prefill_inputs(shape: PrefillShape, seed: int):
+    """q [B,Hq,T,d], k, v [B,Hkv,T,d] on the CPU, iid N(0,1) rounded to shape.dtype."""
+    g = torch.Generator().manual_seed(seed)
+    q = torch.randn(shape.B, shape.Hq, shape.T, shape.d, generator=g)
+    k = torch.randn(shape.B, shape.Hkv, shape.T, shape.d, generator=g)
+    v = torch.randn(shape.B, shape.Hkv, shape.T, shape.d, generator=g)
+    return q.to(shape.dtype), k.to(shape.dtype), v.to(shape.dtype)
+
+
+@dataclass
+class PagedInputs:
+    q: torch.Tensor            # [B, Hq, d]
+    k_pages: torch.Tensor      # [num_pages, Hkv, page_size, d]
+    v_pages: torch.Tensor      # [num_pages, Hkv, page_size, d]
+    block_table: torch.Tensor  # [B, W] int32, unused entries -1
+    seq_lens: torch.Tensor     # [B] int32
+    page_size: int
+
+    @property
+    def max_pages_per_seq(self) -> int:
+        return self.block_table.shape[1]
+
+    def kv_bytes(self) -> int:
+        """Bytes of K and V that valid tokens occupy (unused slots excluded)."""
+        Hkv, d = self.k_pages.shape[1], self.k_pages.shape[3]
+        return 2 * int(self.seq_lens.sum()) * Hkv * d * self.k_pages.element_size()
+
+    def algorithmic_bytes(self) -> int:
+        """K/V of valid tokens + q + out + used block-table entries + seq_lens."""
+        es = self.q.element_size()
+        used_pages = int(((self.seq_lens.long() + self.page_size - 1) // self.page_size).sum())
+        return self.kv_bytes() + 2 * self.q.numel() * es + 4 * used_pages + 4 * self.seq_lens.numel()
+
+
+def _pool_layout(seq_lens, page_size, W, g, extra_pages):
+    """Block table over a pool of exactly sum(ceil(L/page_size)) pages (+ extra), in randperm order."""
+    B = seq_lens.shape[0]
+    npages = (seq_lens + page_size - 1) // page_size
+    used = int(npages.sum())
+    num_pages = used + extra_pages
+    perm = torch.randperm(num_pages, generator=g)
+    table = torch.full((B, W), -1, dtype=torch.int32)
+    off = 0
+    for b in range(B):
+        n = int(npages[b])
+        table[b, :n] = perm[off : off + n].to(torch.int32)
+        off += n
+    return table, num_pages
+
+
+def _poison(pages, table, seq_lens, page_size, extra_pages, value):
+    """Write ``value`` into every slot no valid token occupies."""
+    referenced = torch.zeros(pages.shape[0], dtype=torch.bool)
+    for b in range(table.shape[0]):
+        L = int(seq_lens[b])
+        n = -(-L // page_size)
+        if n:
+            referenced[table[b, :n].long()] = True
+            tail = L - (n - 1) * page_size
+            pages[int(table[b, n - 1]), :, tail:, :] = value
+    pages[~referenced] = value
+
+
+def paged_inputs(shape: DecodeShape, seed: int, *, seq_lens=None, extra_pages=0, poison=None, B=None):
+    """Paged decode inputs: seq_lens ~ U{L_lo..L_hi} (unless given), pool in randperm order.
+
+    ``poison`` (e.g. float('nan')) fills every slot no valid token occupies,
+    including ``extra_pages`` pages that no sequence references.
+    """
+    g = torch.Generator().manual_seed(seed)
+    B = shape.B if B is None else B
+    if seq_lens is None:
+        seq_lens = torch.randint(shape.L_lo, shape.L_hi + 1, (B,), generator=g)
+    seq_lens = torch.as_tensor(seq_lens, dtype=torch.int64)
+    W = shape.max_pages_per_seq
+    table, num_pages = _pool_layout(seq_lens, shape.page_size, W, g, extra_pages)
+    q = torch.randn(B, shape.Hq, shape.d, generator=g).to(shape.dtype)
+    pool_shape = (num_pages, shape.Hkv, shape.page_size, shape.d)
+    k_pages = torch.randn(pool_shape, generator=g).to(shape.dtype)
+    v_pages = torch.randn(pool_shape, generator=g).to(shape.dtype)
+    if poison is not None:
+        _poison(k_pages, table, seq_lens, shape.page_size, extra_pages, poison)
+        _poison(v_pages, table, seq_lens, shape.page_size, extra_pages, poison)
+    return PagedInputs(q, k_pages, v_pages, table, seq_lens.to(torch.int32), shape.page_size)
+
+
+def paged_from_dense(k, v, seq_lens, page_size, seed, W=None, poison=None):
+    """Scatter dense K/V [B,Hkv,T,d] (tokens 0..L_b-1 of each b) into a permuted page pool.
+
+    Returns (k_pages, v_pages, block_table int32, seq_lens int32).
+    """
+    B, Hkv, T, d = k.shape
+    seq_lens = torch.as_tensor(seq_lens, dtype=torch.int64)
+    W = W if W is not None else -(-T // page_size)
+    g = torch.Generator().manual_seed(seed)
+    table, num_pages = _pool_layout(seq_lens, page_size, W, g, 0)
+    fill = float("nan") if poison is None else poison
+    k_pages = torch.full((num_pages, Hkv, page_size, d), fill, dtype=k.dtype)
+    v_pages = torch.full((num_pages, Hkv, page_size, d), fill, dtype=v.dtype)
+    for b in range(B):
+        L = int(seq_lens[b])
+        for j in range(0, L, page_size):
+            n = min(page_size, L - j)
+            p = int(table[b, j // page_size])
+            k_pages[p, :, :n] = k[b, :, j : j + n]
+            v_pages[p, :, :n] = v[b, :, j : j + n]
+    return k_pages, v_pages, table, seq_lens.to(torch.int32)
+
+
+def permute_pages(k_pages, v_pages, block_table, seed):
+    """Same cache under a different physical page order: pages moved, table rewritten."""
+    g = torch.Generator().manual_seed(seed)
+    P = k_pages.shape[0]
+    perm = torch.randperm(P, generator=g)          # new position of old page i is perm[i]
+    inv = torch.empty_like(perm)
+    inv[perm] = torch.arange(P)
+    k2 = k_pages[inv]
+    v2 = v_pages[inv]
+    t2 = block_table.clone()
+    used = t2 >= 0
+    t2[used] = perm[t2[used].long()].to(torch.int32)
+    return k2, v2, t2
+
+
+def fp32_scale(d: int) -> float:
+    """1/sqrt(d) rounded to float32: the value the kernels receive."""
+    return float(torch.tensor(1.0 / math.sqrt(d), dtype=torch.float32))

@@ -1,0 +1,166 @@
+"""fp64 reference attention: causal prefill and paged single-token decode.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring): never imported by the
+product path.
+
+Definition followed (the pages name the operation but print no formula, so
+the plainest reading of "causal multi-head / grouped-query scaled-dot-product
+attention" is written out; every reading is listed with its reason in the
+design notes of the repository):
+
+  for query head h of batch b, with kv head  kv = floor(h / g),  g = Hq / Hkv
+  (GQA as in the microLLM-rocm README, "Why this project exists": decoder-only
+  MHA/GQA causal attention; consecutive query heads share one kv head),
+
+      s_ij   = scale * <q_i, k_j>          for every visible key j
+      m_i    = max_j s_ij
+      p_ij   = exp(s_ij - m_i)             (max subtracted: same value, no overflow)
+      l_i    = sum_j p_ij
+      out_i  = sum_j (p_ij / l_i) v_j
+      lse_i  = m_i + ln l_i                (natural log, scale included)
+
+  Prefill: T queries against the same T keys; query i sees keys 0..i
+  inclusive (the causal mask).  The score matrix is materialised in full and
+  the masked entries set to -inf before the row softmax: the "naive" backend
+  of the RoseLLM README ("Systems highlights", "Inference and serving") and
+  the Softmax / ScaledDotProductAttention primitives of the llm-from-scratch
+  "Project Overview" page ("Core Stack: llm/").
+
+  Paged decode: one query per sequence, standing at position L-1 of a
+  sequence of L = seq_lens[b] cached tokens, so it sees keys 0..L-1 (its own
+  K/V already appended).  Token j lives in physical page
+  block_table[b][j // page_size], slot j % page_size: the paged KV cache of
+  the RoseLLM README ("What is inside"; "Systems highlights", "Inference and
+  serving") and the mapped KV store of the microLLM-rocm README ("Why this
+  project exists").  Slots at or past L are never read.  L == 0 has no
+  visible key: the sum is empty, so lse = ln 0 = -inf, and out is defined
+  as 0.
+
+Arithmetic is NumPy float64 throughout.  Inputs may be any real dtype; bf16
+tensors must be converted by the caller (exactly, via float32) before they
+arrive here.
+"""
+
+import numpy as np
+
+
+def kv_head_of(h, Hq, Hkv):
+    """kv head read by query head ``h``: consecutive groups of g = Hq/Hkv."""
+    if Hkv <= 0 or Hq % Hkv != 0:
+        raise ValueError(f"Hq={Hq} is not a multiple of Hkv={Hkv}")
+    return h // (Hq // Hkv)
+
+
+def _attend(qrows, keys, vals, scale, visible):
+    """Softmax attention of R query rows over N keys, scores materialised.
+
+    qrows [R, d], keys [N, d], vals [N, dv]; visible: bool [R, N], every row
+    with at least one True.  Returns (out [R, dv], lse [R]).
+    """
+    s = scale * (qrows @ keys.T)
+    s = np.where(visible, s, -np.inf)
+    m = s.max(axis=1, keepdims=True)
+    e = np.exp(s - m)
+    l = e.sum(axis=1, keepdims=True)
+    out = (e @ vals) / l
+    lse = m[:, 0] + np.log(l[:, 0])
+    return out, lse
+
+
+def _as64(x):
+    return np.asarray(x, dtype=np.float64)
+
+
+def _check_prefill(q, k, v):
+    if q.ndim != 4 or k.ndim != 4 or v.ndim != 4:
+        raise ValueError("q, k, v must be [B, H, T, d]")
+    B, Hq, T, d = q.shape
+    if k.shape != v.shape or k.shape[0] != B or k.shape[2] != T or k.shape[3] != d:
+        raise ValueError(f"shape mismatch q{q.shape} k{k.shape} v{v.shape}")
+    kv_head_of(0, Hq, k.shape[1])
+    return B, Hq, k.shape[1], T, d
+
+
+def prefill(q, k, v, scale):
+    """Causal prefill.  q [B,Hq,T,d], k/v [B,Hkv,T,d] -> (out [B,Hq,T,d], lse [B,Hq,T])."""
+    q, k, v = _as64(q), _as64(k), _as64(v)
+    B, Hq, Hkv, T, d = _check_prefill(q, k, v)
+    scale = float(scale)
+    visible = np.tril(np.ones((T, T), dtype=bool), k=0)
+    out = np.zeros((B, Hq, T, d))
+    lse = np.zeros((B, Hq, T))
+    if T == 0:
+        return out, lse
+    for b in range(B):
+        for h in range(Hq):
+            kv = kv_head_of(h, Hq, Hkv)
+            out[b, h], lse[b, h] = _attend(q[b, h], k[b, kv], v[b, kv], scale, visible)
+    return out, lse
+
+
+def prefill_rows(q, k, v, scale, b, h, rows):
+    """Selected causal-prefill rows of one (b, h), each row computed on its own.
+
+    Row i attends over keys 0..i only, so only the keys a row can see are
+    touched; used to check outputs sampled from shapes too large for
+    ``prefill``.  Returns (out [len(rows), d], lse [len(rows)]).
+    """
+    Hq, Hkv = q.shape[1], k.shape[1]
+    kv = kv_head_of(h, Hq, Hkv)
+    outs, lses = [], []
+    for i in rows:
+        i = int(i)
+        qi = _as64(q[b, h, i : i + 1])
+        ks = _as64(k[b, kv, : i + 1])
+        vs = _as64(v[b, kv, : i + 1])
+        o, s = _attend(qi, ks, vs, float(scale), np.ones((1, i + 1), dtype=bool))
+        outs.append(o[0])
+        lses.append(s[0])
+    d = q.shape[3]
+    return np.array(outs).reshape(len(outs), d), np.array(lses)
+
+
+def gather_pages(pages, table_row, L, page_size, kvh):
+    """Tokens 0..L-1 of one sequence and kv head, read through its block table.
+
+    pages [num_pages, Hkv, page_size, d]; table_row [max_pages_per_seq].
+    """
+    j = np.arange(L)
+    page_ids = np.asarray(table_row)[j // page_size]
+    slots = j % page_size
+    if np.any(page_ids < 0) or np.any(page_ids >= pages.shape[0]):
+        raise ValueError("block table names a page outside the pool")
+    return _as64(pages[page_ids, kvh, slots])
+
+
+def decode_paged(q, k_pages, v_pages, block_table, seq_lens, scale, page_size):
+    """Single-token decode over a paged KV cache.
+
+    q [B,Hq,d]; k_pages/v_pages [num_pages,Hkv,page_size,d];
+    block_table [B, W] int; seq_lens [B] int.  Returns (out [B,Hq,d], lse [B,Hq]).
+    """
+    q = _as64(q)
+    B, Hq, d = q.shape
+    Hkv = k_pages.shape[1]
+    if k_pages.shape != v_pages.shape or k_pages.shape[2] != page_size or k_pages.shape[3] != d:
+        raise ValueError("page pools must be [num_pages, Hkv, page_size, d]")
+    bt = np.asarray(block_table)
+    sl = np.asarray(seq_lens)
+    if bt.shape[0] != B or sl.shape != (B,):
+        raise ValueError("block_table must be [B, W] and seq_lens [B]")
+    kv_head_of(0, Hq, Hkv)
+    out = np.zeros((B, Hq, d))
+    lse = np.full((B, Hq), -np.inf)
+    for b in range(B):
+        L = int(sl[b])
+        if L < 0 or L > bt.shape[1] * page_size:
+            raise ValueError(f"seq_lens[{b}]={L} outside [0, W*page_size]")
+        if L == 0:
+            continue
+        for h in range(Hq):
+            kv = kv_head_of(h, Hq, Hkv)
+            keys = gather_pages(k_pages, bt[b], L, page_size, kv)
+            vals = gather_pages(v_pages, bt[b], L, page_size, kv)
+            o, s = _attend(q[b, h][None, :], keys, vals, float(scale), np.ones((1, L), dtype=bool))
+            out[b, h], lse[b, h] = o[0], s[0]
+    return out, lse
