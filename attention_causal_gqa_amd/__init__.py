@@ -1,0 +1,27 @@
+"""Causal MHA/GQA attention for MI355X (gfx950): bf16 MFMA prefill and paged split-KV decode.
+
+The compute lives in ``libattn.so`` (hand-written HIP kernels behind the C ABI
+declared in ``include/attn.h``); this package is its ctypes binding, with the
+same function names.  ``synth`` draws the seeded synthetic inputs the tests and
+the benchmark use.
+"""
+
+from ._binding import (  # noqa: F401
+    ATTN_BF16,
+    ATTN_ERR_HIP,
+    ATTN_ERR_INVALID_ARG,
+    ATTN_ERR_UNSUPPORTED,
+    ATTN_ERR_WORKSPACE,
+    ATTN_F32,
+    ATTN_OK,
+    LIB_PATH,
+    AttnError,
+    attn_decode_num_splits,
+    attn_decode_paged,
+    attn_decode_workspace_bytes,
+    attn_last_error_message,
+    attn_prefill,
+    attn_status_string,
+    attn_validate_paged_metadata,
+    load_library,
+)

@@ -1,0 +1,195 @@
+"""ctypes binding of libattn.so: same names as the C ABI, argument marshalling only.
+
+Every step of the computation runs in the HIP kernels behind the C ABI;
+this module turns torch tensors into pointers and sizes, picks the current
+HIP stream, allocates outputs or workspace with torch when the caller gives
+none, and raises ``AttnError`` on a non-zero status.  If the library is not
+built, every call raises: there is no other path.
+"""
+
+import ctypes
+import math
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libattn.so")
+
+ATTN_OK = 0
+ATTN_ERR_INVALID_ARG = -1
+ATTN_ERR_UNSUPPORTED = -2
+ATTN_ERR_WORKSPACE = -3
+ATTN_ERR_HIP = -4
+
+ATTN_F32 = 0
+ATTN_BF16 = 1
+
+_lib = None
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"{message} (status {status})")
+        self.status = status
+
+
+def load_library():
+    """The ctypes handle of libattn.so, with argument types declared."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise AttnError(ATTN_ERR_HIP, f"{LIB_PATH} is not built; run `python -m attention_causal_gqa_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.attn_prefill.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, vp]
+    lib.attn_prefill.restype = i32
+    lib.attn_decode_num_splits.argtypes = [i32] * 7
+    lib.attn_decode_num_splits.restype = i32
+    lib.attn_decode_workspace_bytes.argtypes = [i32] * 7
+    lib.attn_decode_workspace_bytes.restype = sz
+    lib.attn_decode_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, i32, i32,
+                                      vp, sz, vp]
+    lib.attn_decode_paged.restype = i32
+    lib.attn_validate_paged_metadata.argtypes = [vp, vp, i32, i32, i32, i32]
+    lib.attn_validate_paged_metadata.restype = i32
+    lib.attn_status_string.argtypes = [i32]
+    lib.attn_status_string.restype = ctypes.c_char_p
+    lib.attn_last_error_message.argtypes = []
+    lib.attn_last_error_message.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def attn_status_string(status):
+    return load_library().attn_status_string(status).decode()
+
+
+def attn_last_error_message():
+    return load_library().attn_last_error_message().decode()
+
+
+def _check(status):
+    if status != ATTN_OK:
+        raise AttnError(status, f"{attn_status_string(status)}: {attn_last_error_message()}")
+
+
+def _torch():
+    import torch
+
+    return torch
+
+
+def _dtype_code(t):
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return ATTN_F32
+    if t.dtype == torch.bfloat16:
+        return ATTN_BF16
+    raise AttnError(ATTN_ERR_UNSUPPORTED, f"dtype {t.dtype} is not supported")
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream):
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    return _torch().cuda.current_stream().cuda_stream
+
+
+def _require(cond, msg):
+    if not cond:
+        raise AttnError(ATTN_ERR_INVALID_ARG, msg)
+
+
+def _dense_on_gpu(name, t):
+    _require(t.is_cuda, f"{name} must be a GPU tensor")
+    _require(t.is_contiguous(), f"{name} must be contiguous")
+
+
+def attn_prefill(q, k, v, out=None, lse=None, scale=None, stream=None):
+    """Causal prefill.  q [B,Hq,T,d], k/v [B,Hkv,T,d] (bf16 or fp32) -> (out, lse fp32 [B,Hq,T])."""
+    torch = _torch()
+    _require(q.dim() == 4 and k.dim() == 4 and v.dim() == 4, "q, k, v must be [B, H, T, d]")
+    B, Hq, T, d = q.shape
+    Hkv = k.shape[1]
+    _require(k.shape == v.shape and k.shape[0] == B and k.shape[2] == T and k.shape[3] == d, "k/v shape mismatch")
+    _require(q.dtype == k.dtype == v.dtype, "q, k, v must share a dtype")
+    for n, t in (("q", q), ("k", k), ("v", v)):
+        _dense_on_gpu(n, t)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hq, T), dtype=torch.float32, device=q.device)
+    _dense_on_gpu("out", out)
+    _require(out.shape == q.shape and out.dtype == q.dtype, "out must match q")
+    if lse is not False:
+        _dense_on_gpu("lse", lse)
+        _require(lse.shape == (B, Hq, T) and lse.dtype == torch.float32, "lse must be float32 [B, Hq, T]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    lib = load_library()
+    _check(lib.attn_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(out), None if lse is False else _ptr(lse),
+                            B, Hq, Hkv, T, d, float(scale), _dtype_code(q), _stream(stream)))
+    return out, (None if lse is False else lse)
+
+
+def attn_decode_num_splits(B, Hq, Hkv, d, page_size, max_pages_per_seq, num_splits=0):
+    s = load_library().attn_decode_num_splits(B, Hq, Hkv, d, page_size, max_pages_per_seq, num_splits)
+    _check(min(s, 0))
+    return s
+
+
+def attn_decode_workspace_bytes(B, Hq, Hkv, d, page_size, max_pages_per_seq, num_splits=0):
+    return load_library().attn_decode_workspace_bytes(B, Hq, Hkv, d, page_size, max_pages_per_seq, num_splits)
+
+
+def attn_decode_paged(q, k_pages, v_pages, block_table, seq_lens, out=None, lse=None, scale=None, num_splits=0,
+                      workspace=None, stream=None):
+    """Paged single-token decode.  q [B,Hq,d]; pools [P,Hkv,page,d]; block_table [B,W] int32; seq_lens [B] int32."""
+    torch = _torch()
+    _require(q.dim() == 3 and k_pages.dim() == 4 and k_pages.shape == v_pages.shape, "bad q / page pool shapes")
+    B, Hq, d = q.shape
+    P, Hkv, page_size, dk = k_pages.shape
+    _require(dk == d, "page pools and q disagree on d")
+    _require(block_table.dim() == 2 and block_table.shape[0] == B and block_table.dtype == torch.int32,
+             "block_table must be int32 [B, W]")
+    _require(seq_lens.shape == (B,) and seq_lens.dtype == torch.int32, "seq_lens must be int32 [B]")
+    for n, t in (("q", q), ("k_pages", k_pages), ("v_pages", v_pages), ("block_table", block_table),
+                 ("seq_lens", seq_lens)):
+        _dense_on_gpu(n, t)
+    _require(q.dtype == k_pages.dtype == v_pages.dtype, "q and the page pools must share a dtype")
+    W = block_table.shape[1]
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    _dense_on_gpu("out", out)
+    _require(out.shape == q.shape and out.dtype == q.dtype, "out must match q")
+    if lse is not False:
+        _dense_on_gpu("lse", lse)
+        _require(lse.shape == (B, Hq) and lse.dtype == torch.float32, "lse must be float32 [B, Hq]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    lib = load_library()
+    need = lib.attn_decode_workspace_bytes(B, Hq, Hkv, d, page_size, W, num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _dense_on_gpu("workspace", workspace)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib.attn_decode_paged(_ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table), _ptr(seq_lens), _ptr(out),
+                                 None if lse is False else _ptr(lse), B, Hq, Hkv, d, page_size, P, W, float(scale),
+                                 _dtype_code(q), num_splits, _ptr(workspace), ws_bytes, _stream(stream)))
+    return out, (None if lse is False else lse)
+
+
+def attn_validate_paged_metadata(block_table, seq_lens, page_size, num_pages):
+    """Host check of paged metadata (CPU int32 tensors or arrays); raises AttnError if out of contract."""
+    import numpy as np
+
+    bt = np.ascontiguousarray(np.asarray(block_table.cpu() if hasattr(block_table, "cpu") else block_table,
+                                         dtype=np.int32))
+    sl = np.ascontiguousarray(np.asarray(seq_lens.cpu() if hasattr(seq_lens, "cpu") else seq_lens, dtype=np.int32))
+    B, W = bt.shape
+    _check(load_library().attn_validate_paged_metadata(bt.ctypes.data, sl.ctypes.data, B, W, page_size, num_pages))

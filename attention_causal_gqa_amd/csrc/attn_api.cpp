@@ -1,0 +1,207 @@
+// C-ABI host layer: argument validation, split planning, workspace sizing and
+// dispatch to the HIP kernels.  Every check runs before any HIP call, so a
+// rejected call has no device side effect and can be tested without a GPU.
+// Unsupported-but-valid requests are reported as such, never served by a
+// fallback (the microLLM-rocm README, "Why this project exists", keeps
+// unsupported rows explicit; "The design keeps three implementations":
+// an optimised path honours the same shape and error contracts).
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <string>
+
+#include "../../include/attn.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int status, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return status;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int from_hip(hipError_t e, const char* what) {
+    if (e == hipSuccess) return ATTN_OK;
+    return fail(ATTN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr int kPageSize = 16;
+constexpr int kMaxDecodeGroup = 8;
+constexpr int kMaxPrefillGroup = 128;
+constexpr int64_t kMaxGrid = 0x7fffffff;
+
+// ---- decode split plan ------------------------------------------------------
+struct Plan {
+    int splits;
+    int pages_per_split;
+};
+
+// Automatic plan: the largest pages-per-split in {16, 8, 4} that still gives
+// at least 4096 workgroups (16 per CU on 256 CUs), so that sequences of very
+// different lengths even out across the chip; never fewer than 4 pages per
+// split, to keep partial-result traffic small next to the K/V stream.
+Plan make_plan(int B, int Hkv, int W, int num_splits) {
+    Plan p{};
+    if (num_splits > 0) {
+        const int s = num_splits < W ? num_splits : W;
+        p.pages_per_split = (W + s - 1) / s;
+    } else {
+        int pps = 16;
+        while (pps > 4 && (int64_t)B * Hkv * ((W + pps - 1) / pps) < 4096) pps /= 2;
+        p.pages_per_split = pps;
+    }
+    p.splits = (W + p.pages_per_split - 1) / p.pages_per_split;
+    return p;
+}
+
+size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t workspace_for(int B, int Hq, int d, const Plan& p) {
+    const size_t n = (size_t)B * Hq * p.splits;
+    return round256(n * d * sizeof(float)) + round256(n * sizeof(float));
+}
+
+int check_decode_sizes(int B, int Hq, int Hkv, int d, int page_size, int W, int num_splits) {
+    if (B < 0) return fail(ATTN_ERR_INVALID_ARG, "B=%d must be >= 0", B);
+    if (Hq < 1 || Hkv < 1) return fail(ATTN_ERR_INVALID_ARG, "Hq=%d, Hkv=%d must be >= 1", Hq, Hkv);
+    if (Hq % Hkv != 0) return fail(ATTN_ERR_INVALID_ARG, "Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
+    if (d < 1) return fail(ATTN_ERR_INVALID_ARG, "d=%d must be >= 1", d);
+    if (page_size < 1) return fail(ATTN_ERR_INVALID_ARG, "page_size=%d must be >= 1", page_size);
+    if (W < 1) return fail(ATTN_ERR_INVALID_ARG, "max_pages_per_seq=%d must be >= 1", W);
+    if (num_splits < 0) return fail(ATTN_ERR_INVALID_ARG, "num_splits=%d must be >= 0", num_splits);
+    if ((int64_t)W * page_size > 0x7fffffff) return fail(ATTN_ERR_INVALID_ARG, "max_pages_per_seq * page_size overflows int");
+    if (d != 64 && d != 128) return fail(ATTN_ERR_UNSUPPORTED, "decode supports d = 64 or 128, not %d", d);
+    if (page_size != kPageSize) return fail(ATTN_ERR_UNSUPPORTED, "decode supports page_size = 16, not %d", page_size);
+    if (Hq / Hkv > kMaxDecodeGroup)
+        return fail(ATTN_ERR_UNSUPPORTED, "decode supports Hq/Hkv <= %d, not %d", kMaxDecodeGroup, Hq / Hkv);
+    return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* attn_status_string(int status) {
+    switch (status) {
+        case ATTN_OK: return "ATTN_OK";
+        case ATTN_ERR_INVALID_ARG: return "ATTN_ERR_INVALID_ARG: invalid argument";
+        case ATTN_ERR_UNSUPPORTED: return "ATTN_ERR_UNSUPPORTED: valid request with no kernel in this build";
+        case ATTN_ERR_WORKSPACE: return "ATTN_ERR_WORKSPACE: workspace missing or too small";
+        case ATTN_ERR_HIP: return "ATTN_ERR_HIP: HIP runtime error";
+        default: return "unknown attn status";
+    }
+}
+
+const char* attn_last_error_message(void) { return g_last_error.c_str(); }
+
+int attn_prefill(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Hq, int Hkv, int T,
+                 int d, float scale, attn_dtype_t dtype, hipStream_t stream) {
+    g_last_error.clear();
+    if (dtype != ATTN_F32 && dtype != ATTN_BF16) return fail(ATTN_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
+    if (B < 0 || T < 0) return fail(ATTN_ERR_INVALID_ARG, "B=%d, T=%d must be >= 0", B, T);
+    if (Hq < 1 || Hkv < 1) return fail(ATTN_ERR_INVALID_ARG, "Hq=%d, Hkv=%d must be >= 1", Hq, Hkv);
+    if (Hq % Hkv != 0) return fail(ATTN_ERR_INVALID_ARG, "Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
+    if (d < 1) return fail(ATTN_ERR_INVALID_ARG, "d=%d must be >= 1", d);
+    if (!std::isfinite(scale)) return fail(ATTN_ERR_INVALID_ARG, "scale must be finite");
+    if (d != 64 && d != 128) return fail(ATTN_ERR_UNSUPPORTED, "prefill supports d = 64 or 128, not %d", d);
+    if (dtype == ATTN_BF16 && Hq / Hkv > kMaxPrefillGroup)
+        return fail(ATTN_ERR_UNSUPPORTED, "bf16 prefill supports Hq/Hkv <= %d", kMaxPrefillGroup);
+    if (B == 0 || T == 0) return ATTN_OK;
+    if (!q || !k || !v || !out) return fail(ATTN_ERR_INVALID_ARG, "q, k, v and out must be non-null");
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16))
+        return fail(ATTN_ERR_INVALID_ARG, "q, k, v and out must be 16-byte aligned");
+    if (lse && !aligned(lse, 4)) return fail(ATTN_ERR_INVALID_ARG, "lse must be 4-byte aligned");
+    // Grid and element counts must fit the kernels' index arithmetic.
+    const int64_t rows_per_block = dtype == ATTN_F32 ? 64 : (128 / (Hq / Hkv));
+    const int64_t nqb = (T + rows_per_block - 1) / rows_per_block;
+    const int64_t blocks = nqb * B * (dtype == ATTN_F32 ? Hq : Hkv);
+    if (blocks > kMaxGrid) return fail(ATTN_ERR_INVALID_ARG, "problem too large: %lld workgroups", (long long)blocks);
+
+    attn::PrefillArgs a{q, k, v, out, lse, B, Hq, Hkv, T, d, scale};
+    hipError_t e = dtype == ATTN_F32 ? attn::launch_prefill_f32(a, stream) : attn::launch_prefill_bf16(a, stream);
+    return from_hip(e, "attn_prefill launch");
+}
+
+int attn_decode_num_splits(int B, int Hq, int Hkv, int d, int page_size, int max_pages_per_seq, int num_splits) {
+    g_last_error.clear();
+    int st = check_decode_sizes(B, Hq, Hkv, d, page_size, max_pages_per_seq, num_splits);
+    if (st != ATTN_OK) return st;
+    return make_plan(B, Hkv, max_pages_per_seq, num_splits).splits;
+}
+
+size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int d, int page_size, int max_pages_per_seq,
+                                   int num_splits) {
+    g_last_error.clear();
+    if (check_decode_sizes(B, Hq, Hkv, d, page_size, max_pages_per_seq, num_splits) != ATTN_OK) return 0;
+    return workspace_for(B, Hq, d, make_plan(B, Hkv, max_pages_per_seq, num_splits));
+}
+
+int attn_decode_paged(const void* q, const void* k_pages, const void* v_pages, const int32_t* block_table,
+                      const int32_t* seq_lens, void* out, float* lse, int B, int Hq, int Hkv, int d, int page_size,
+                      int num_pages, int max_pages_per_seq, float scale, attn_dtype_t dtype, int num_splits,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    g_last_error.clear();
+    if (dtype != ATTN_F32 && dtype != ATTN_BF16) return fail(ATTN_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
+    int st = check_decode_sizes(B, Hq, Hkv, d, page_size, max_pages_per_seq, num_splits);
+    if (st != ATTN_OK) return st;
+    if (num_pages < 0) return fail(ATTN_ERR_INVALID_ARG, "num_pages=%d must be >= 0", num_pages);
+    if (!std::isfinite(scale)) return fail(ATTN_ERR_INVALID_ARG, "scale must be finite");
+    if (dtype != ATTN_BF16) return fail(ATTN_ERR_UNSUPPORTED, "decode supports ATTN_BF16 only");
+    if (B == 0) return ATTN_OK;
+    if (!q || !k_pages || !v_pages || !block_table || !seq_lens || !out)
+        return fail(ATTN_ERR_INVALID_ARG, "q, k_pages, v_pages, block_table, seq_lens and out must be non-null");
+    if (!aligned(q, 16) || !aligned(k_pages, 16) || !aligned(v_pages, 16) || !aligned(out, 16))
+        return fail(ATTN_ERR_INVALID_ARG, "q, k_pages, v_pages and out must be 16-byte aligned");
+    if (!aligned(block_table, 4) || !aligned(seq_lens, 4) || (lse && !aligned(lse, 4)))
+        return fail(ATTN_ERR_INVALID_ARG, "block_table, seq_lens and lse must be 4-byte aligned");
+
+    const Plan plan = make_plan(B, Hkv, max_pages_per_seq, num_splits);
+    if ((int64_t)plan.splits * Hkv * B > kMaxGrid) return fail(ATTN_ERR_INVALID_ARG, "problem too large");
+    const size_t need = workspace_for(B, Hq, d, plan);
+    if (!workspace || workspace_bytes < need)
+        return fail(ATTN_ERR_WORKSPACE, "workspace %zu bytes given, %zu needed", workspace ? workspace_bytes : 0, need);
+    if (!aligned(workspace, 16)) return fail(ATTN_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+
+    const size_t n = (size_t)B * Hq * plan.splits;
+    float* o_part = static_cast<float*>(workspace);
+    float* lse_part = reinterpret_cast<float*>(static_cast<char*>(workspace) + round256(n * d * sizeof(float)));
+    attn::DecodeArgs a{q,      k_pages,  v_pages, block_table, seq_lens, out, lse, o_part, lse_part, B,
+                       Hq,     Hkv,      d,       page_size,   max_pages_per_seq, plan.splits,
+                       plan.pages_per_split, scale};
+    return from_hip(attn::launch_decode_bf16(a, stream), "attn_decode_paged launch");
+}
+
+int attn_validate_paged_metadata(const int32_t* block_table_host, const int32_t* seq_lens_host, int B,
+                                 int max_pages_per_seq, int page_size, int num_pages) {
+    g_last_error.clear();
+    if (B < 0 || max_pages_per_seq < 1 || page_size < 1 || num_pages < 0)
+        return fail(ATTN_ERR_INVALID_ARG, "bad sizes: B=%d W=%d page_size=%d num_pages=%d", B, max_pages_per_seq,
+                    page_size, num_pages);
+    if (B == 0) return ATTN_OK;
+    if (!block_table_host || !seq_lens_host) return fail(ATTN_ERR_INVALID_ARG, "null metadata pointer");
+    const int64_t cap = (int64_t)max_pages_per_seq * page_size;
+    for (int b = 0; b < B; ++b) {
+        const int L = seq_lens_host[b];
+        if (L < 0 || L > cap) return fail(ATTN_ERR_INVALID_ARG, "seq_lens[%d]=%d outside [0, %lld]", b, L, (long long)cap);
+        const int used = (L + page_size - 1) / page_size;
+        for (int j = 0; j < used; ++j) {
+            const int pid = block_table_host[(size_t)b * max_pages_per_seq + j];
+            if (pid < 0 || pid >= num_pages)
+                return fail(ATTN_ERR_INVALID_ARG, "block_table[%d][%d]=%d outside [0, %d)", b, j, pid, num_pages);
+        }
+    }
+    return ATTN_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,40 @@
+// Internal launch interface between the C-ABI host layer (attn_api.cpp) and
+// the HIP kernels.  Arguments arrive here already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+struct PrefillArgs {
+    const void* q;   // [B, Hq, T, d]
+    const void* k;   // [B, Hkv, T, d]
+    const void* v;   // [B, Hkv, T, d]
+    void* out;       // [B, Hq, T, d]
+    float* lse;      // [B, Hq, T] or nullptr
+    int B, Hq, Hkv, T, d;
+    float scale;
+};
+
+struct DecodeArgs {
+    const void* q;            // [B, Hq, d]
+    const void* k_pages;      // [num_pages, Hkv, page_size, d]
+    const void* v_pages;      // [num_pages, Hkv, page_size, d]
+    const int32_t* block_table;  // [B, W]
+    const int32_t* seq_lens;     // [B]
+    void* out;                // [B, Hq, d]
+    float* lse;               // [B, Hq] or nullptr
+    float* o_part;            // workspace [B, Hq, S, d]
+    float* lse_part;          // workspace [B, Hq, S]
+    int B, Hq, Hkv, d, page_size, W;
+    int num_splits;           // S
+    int pages_per_split;
+    float scale;
+};
+
+hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t stream);
+hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream);
+hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream);
+
+}  // namespace attn

@@ -1,0 +1,301 @@
+// Causal GQA prefill, bf16 inputs, fp32 accumulation, on gfx950 MFMA.
+//
+// Method: blockwise online softmax (llm-from-scratch "Project Overview",
+// "Performance Layer: kernel/ and parallel/"): scores are produced one key
+// tile at a time and folded into running row statistics, so the T x T score
+// matrix is never stored.  Causal MHA/GQA with BF16 data and FP32
+// accumulation as named in the microLLM-rocm README ("Why this project
+// exists").
+//
+// Work decomposition (one workgroup = 4 waves = 256 threads):
+//   * A workgroup owns 128 query rows of one (batch, kv head).  The rows are
+//     (token, head) pairs: BMt = floor(128 / G) consecutive tokens times the
+//     G query heads that share the kv head, so every K/V tile staged in LDS
+//     serves all G heads (GQA packing).  Wave w owns rows 32w .. 32w+31.
+//   * Keys are visited in tiles of 64, from key 0 up to the workgroup's last
+//     token; only the tiles that reach past the first token need the causal
+//     mask, applied per element.
+//   * Scores are computed transposed, S^T = K Q^T, with
+//     v_mfma_f32_32x32x16_bf16 (A = K from LDS, B = Q^T held in registers):
+//     in the 32x32 accumulator layout each lane then holds 16 keys of one
+//     query column and lane l ^ 32 holds the other 16, so a row max or sum
+//     is 15 in-lane operations plus one v_permlane32_swap.
+//   * The same accumulator registers, rounded to bf16, are exactly the B
+//     operand of O^T += V^T P^T (the contraction index is relabelled to the
+//     key order the accumulator layout gives).  V is written into LDS
+//     transposed (V^T, d-major) so the A operand is two 8-byte LDS reads.
+//   * out is normalised by the sum of the same bf16-rounded probabilities
+//     that feed the PV product (v_dot2 with ones), so the weights applied to
+//     V sum exactly to the normaliser; the log-sum-exp uses the fp32 sum.
+//   * The running max is only moved when a tile's max exceeds it by more
+//     than 8 (a factor 256 in base 2): rescaling O is then rare, and
+//     probabilities stay below 256, well inside fp32 and bf16 range.
+//   * K/V tiles are double-buffered in LDS: the next tile's global loads are
+//     in flight while the current tile is multiplied.
+//   * Workgroups are launched heaviest first (last query blocks have the
+//     most keys); consecutive workgroup ids cycle over (batch, kv head) so a
+//     kv head's blocks fall on the same XCD and share its L2.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace attn {
+namespace {
+
+constexpr int kRows = 128;  // query rows (token, head pairs) per workgroup
+constexpr int kBN = 64;     // keys per tile
+
+template <int D, bool kPosScale>
+__global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
+                                                              const bf16* __restrict__ v, bf16* __restrict__ out,
+                                                              float* __restrict__ lse, int B, int Hq, int Hkv, int T,
+                                                              int G, int BMt, int nqb, float c1) {
+    constexpr int KS = D + 8;      // bf16 per K row in LDS (16-byte pad: conflict-free 16-byte reads)
+    constexpr int VS = kBN + 4;    // bf16 per V^T row in LDS (8-byte pad)
+    constexpr int CPR = D / 8;     // 16-byte chunks per key row
+    constexpr int KPT = D / 32;    // keys per thread in a tile load
+    constexpr int NKK = D / 16;    // k-steps of QK^T
+    constexpr int NMB = D / 32;    // 32-row blocks of O^T
+    __shared__ __attribute__((aligned(16))) bf16 Ks[2][kBN * KS];
+    __shared__ __attribute__((aligned(16))) bf16 Vt[2][D * VS];
+
+    const int tid = threadIdx.x;
+    const int w = tid >> 6;
+    const int lane = tid & 63;
+    const int l32 = lane & 31;
+    const int hi = lane >> 5;
+
+    const int pairs = B * Hkv;
+    const int qb = nqb - 1 - (int)blockIdx.x / pairs;
+    const int pair = (int)blockIdx.x % pairs;
+    const int b = pair / Hkv;
+    const int kvh = pair % Hkv;
+    const int t0 = qb * BMt;
+
+    // This lane's query column: row r of the workgroup.
+    const int r = 32 * w + l32;
+    const int tt = r / G;
+    const int head = kvh * G + (r % G);
+    const int token = t0 + tt;
+    const bool row_ok = tt < BMt && token < T;
+    const int token_ld = row_ok ? token : t0;  // dead rows compute on a valid row, never stored
+
+    // Q^T as the B operand: lane holds Q[row][16kk + 8hi .. +7].
+    bf16x8 qreg[NKK];
+    {
+        const bf16* qrow = q + ((size_t)(b * Hq + head) * T + token_ld) * D + 8 * hi;
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) qreg[kk] = *reinterpret_cast<const bf16x8*>(qrow + 16 * kk);
+    }
+
+    // Tile-load role: keys kg*KPT .. +KPT-1, 16-byte chunk c of each.
+    const int kg = tid / CPR;
+    const int c = tid % CPR;
+    const bf16* kbase = k + (size_t)(b * Hkv + kvh) * T * D;
+    const bf16* vbase = v + (size_t)(b * Hkv + kvh) * T * D;
+    uint4 kr[KPT], vr[KPT];
+
+    auto gload = [&](int k0) {
+#pragma unroll
+        for (int i = 0; i < KPT; ++i) {
+            const int key = k0 + kg * KPT + i;
+            if (key < T) {
+                kr[i] = *reinterpret_cast<const uint4*>(kbase + (size_t)key * D + 8 * c);
+                vr[i] = *reinterpret_cast<const uint4*>(vbase + (size_t)key * D + 8 * c);
+            } else {
+                kr[i] = make_uint4(0, 0, 0, 0);
+                vr[i] = make_uint4(0, 0, 0, 0);
+            }
+        }
+    };
+    auto lstore = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < KPT; ++i)
+            *reinterpret_cast<uint4*>(&Ks[buf][(kg * KPT + i) * KS + 8 * c]) = kr[i];
+        // V^T[d][key]: element e of chunk c is d = 8c + e; gather it from the KPT keys.
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            uint32_t wv[KPT];
+#pragma unroll
+            for (int i = 0; i < KPT; ++i) {
+                const uint32_t word = (e >> 1) == 0 ? vr[i].x : (e >> 1) == 1 ? vr[i].y : (e >> 1) == 2 ? vr[i].z : vr[i].w;
+                wv[i] = (e & 1) ? (word >> 16) : (word & 0xffffu);
+            }
+            bf16* dst = &Vt[buf][(8 * c + e) * VS + kg * KPT];
+            if constexpr (KPT == 4) {
+                *reinterpret_cast<uint2*>(dst) = make_uint2(wv[0] | (wv[1] << 16), wv[2] | (wv[3] << 16));
+            } else {
+                *reinterpret_cast<uint32_t*>(dst) = wv[0] | (wv[1] << 16);
+            }
+        }
+    };
+
+    f32x16 oacc[NMB];
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[mb][i] = 0.f;
+    float m_run = -INFINITY;  // running max, base-2 scaled domain
+    float l_run = 0.f;        // this lane's share of the row sum of bf16-rounded p (normalises out)
+    float l_lse = 0.f;        // the same sum over fp32 p (for the log-sum-exp)
+
+    const float cc = kPosScale ? c1 : 1.f;
+    const int kend = min(t0 + BMt, T);
+    const int ntiles = (kend + kBN - 1) / kBN;
+    constexpr uint32_t kOnes = 0x3F803F80u;  // two bf16 1.0
+
+    gload(0);
+    lstore(0);
+    __syncthreads();
+
+    for (int t = 0; t < ntiles; ++t) {
+        const int cur = t & 1;
+        const int k0 = t * kBN;
+        if (t + 1 < ntiles) gload(k0 + kBN);
+
+        const bf16* Kc = Ks[cur];
+        const bf16* Vc = Vt[cur];
+
+        // S^T tile (64 keys x 32 query columns) as two 32x32 blocks.
+        f32x16 sacc[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) sacc[kb][i] = 0.f;
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                const bf16x8 a = *reinterpret_cast<const bf16x8*>(Kc + (32 * kb + l32) * KS + 16 * kk + 8 * hi);
+                sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[kk], sacc[kb], 0, 0, 0);
+            }
+        }
+
+        if constexpr (!kPosScale) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) sacc[kb][i] *= c1;
+        }
+        // Causal mask on tiles that reach past the workgroup's first token.
+        // Element i of block kb is key k0 + 32kb + 8(i/4) + 4hi + i%4.
+        if (k0 + kBN - 1 > t0) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int key = k0 + 32 * kb + 8 * (i >> 2) + 4 * hi + (i & 3);
+                    if (key > token) sacc[kb][i] = -INFINITY;
+                }
+        }
+
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
+        mx = pair_max(mx);
+        const float mt = mx * cc;  // tile max in the base-2 domain
+        // Key 0 lies in tile 0 and is visible to every row, so after tile 0
+        // m_run is finite; in tile 0 every lane needs the update.  The branch
+        // is taken by the whole wave, but a lane that does not need it keeps
+        // its max (alpha = 1, exact), so a row's result never depends on the
+        // other rows of its wave.
+        const bool grow = mt > m_run + 8.f;
+        if (__any(grow)) {
+            const float mn = grow ? mt : m_run;
+            const float alpha = fast_exp2(m_run - mn);
+            l_run *= alpha;
+            l_lse *= alpha;
+#pragma unroll
+            for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) oacc[mb][i] *= alpha;
+            m_run = mn;
+        }
+
+        // P^T in bf16: B operand of the PV product.  Two row sums: over the
+        // rounded values (so the weights applied to V sum exactly to the
+        // normaliser of out) and over the fp32 values (the log-sum-exp, which
+        // bf16 rounding of p would otherwise shift by up to 2^-9 relative).
+        uint32_t pb[2][2][4];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    const float p0 = fast_exp2(fmaf(sacc[kb][8 * kc + 2 * jj], cc, -m_run));
+                    const float p1 = fast_exp2(fmaf(sacc[kb][8 * kc + 2 * jj + 1], cc, -m_run));
+                    pb[kb][kc][jj] = pack_bf16x2(p0, p1);
+                    l_run = dot2_bf16(pb[kb][kc][jj], kOnes, l_run);
+                    l_lse += p0 + p1;
+                }
+
+        // O^T (d x 32 queries) += V^T (d x 64 keys) P^T (64 keys x 32 queries).
+        // B element j of (kb, kc) is key 32kb + 16kc + 8(j/4) + 4hi + j%4; the
+        // A operand reads V^T at the same keys.
+#pragma unroll
+        for (int mb = 0; mb < NMB; ++mb) {
+            const bf16* vrow = Vc + (32 * mb + l32) * VS + 4 * hi;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int kc = 0; kc < 2; ++kc) {
+                    const uint2 lo = *reinterpret_cast<const uint2*>(vrow + 32 * kb + 16 * kc);
+                    const uint2 hv = *reinterpret_cast<const uint2*>(vrow + 32 * kb + 16 * kc + 8);
+                    const uint4 av = make_uint4(lo.x, lo.y, hv.x, hv.y);
+                    const uint4 bv = make_uint4(pb[kb][kc][0], pb[kb][kc][1], pb[kb][kc][2], pb[kb][kc][3]);
+                    oacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av),
+                                                                       __builtin_bit_cast(bf16x8, bv), oacc[mb], 0, 0, 0);
+                }
+        }
+
+        if (t + 1 < ntiles) lstore(cur ^ 1);
+        __syncthreads();
+    }
+
+    // Epilogue: lanes l and l^32 hold halves of the row sum.
+    const float lt = pair_sum(l_run);
+    const float ll = pair_sum(l_lse);
+    if (row_ok) {
+        const float inv = 1.f / lt;
+        bf16* orow = out + ((size_t)(b * Hq + head) * T + token) * D + 4 * hi;
+        // O^T element i of block mb is d = 32mb + 8(i/4) + 4hi + i%4.
+#pragma unroll
+        for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                const uint2 wv = make_uint2(pack_bf16x2(oacc[mb][4 * g4] * inv, oacc[mb][4 * g4 + 1] * inv),
+                                            pack_bf16x2(oacc[mb][4 * g4 + 2] * inv, oacc[mb][4 * g4 + 3] * inv));
+                *reinterpret_cast<uint2*>(orow + 32 * mb + 8 * g4) = wv;
+            }
+        if (lse != nullptr && hi == 0) lse[(size_t)(b * Hq + head) * T + token] = (m_run + log2f(ll)) * kLn2;
+    }
+}
+
+template <int D>
+hipError_t launch_d(const PrefillArgs& a, hipStream_t stream) {
+    const int G = a.Hq / a.Hkv;
+    const int BMt = kRows / G;
+    const int nqb = (a.T + BMt - 1) / BMt;
+    const dim3 grid((unsigned)nqb * a.B * a.Hkv);
+    const float c1 = (float)((double)a.scale * 1.4426950408889634);
+    if (c1 > 0.f) {
+        hipLaunchKernelGGL((prefill_bf16_kernel<D, true>), grid, dim3(256), 0, stream, (const bf16*)a.q,
+                           (const bf16*)a.k, (const bf16*)a.v, (bf16*)a.out, a.lse, a.B, a.Hq, a.Hkv, a.T, G, BMt,
+                           nqb, c1);
+    } else {
+        hipLaunchKernelGGL((prefill_bf16_kernel<D, false>), grid, dim3(256), 0, stream, (const bf16*)a.q,
+                           (const bf16*)a.k, (const bf16*)a.v, (bf16*)a.out, a.lse, a.B, a.Hq, a.Hkv, a.T, G, BMt,
+                           nqb, c1);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream) {
+    return a.d == 128 ? launch_d<128>(a, stream) : launch_d<64>(a, stream);
+}
+
+}  // namespace attn

@@ -1,0 +1,158 @@
+/*
+ * attn.h — causal multi-head / grouped-query attention for MI355X (gfx950).
+ *
+ * Two operations, both hand-written HIP kernels behind a plain C ABI:
+ *
+ *  - attn_prefill: causal self-attention of T queries over the same T keys,
+ *    computed block by block with an online softmax so that the T x T score
+ *    matrix never exists in memory (the blockwise softmax-statistics method
+ *    of the llm-from-scratch "Project Overview" page, "Performance Layer:
+ *    kernel/ and parallel/"; causal MHA/GQA as in the microLLM-rocm README,
+ *    "Why this project exists").
+ *
+ *  - attn_decode_paged: one new query token per sequence attending over that
+ *    sequence's cached keys and values, which live in fixed-size pages of a
+ *    shared pool addressed through a per-sequence block table (the paged KV
+ *    cache of the RoseLLM README, "What is inside" and "Systems highlights",
+ *    "Inference and serving"; KV-cache decode with BF16 storage and FP32
+ *    accumulation as in the microLLM-rocm README, "Why this project exists").
+ *    It runs as a split-KV kernel writing partial results, followed by a
+ *    log-sum-exp combine kernel.
+ *
+ * What is computed.  For query head h, the kv head read is h / (Hq / Hkv)
+ * (consecutive groups of query heads share one kv head).  For a query q and
+ * its visible keys k_j with values v_j:
+ *     s_j = scale * <q, k_j>,   out = sum_j softmax(s)_j v_j,
+ *     lse = ln sum_j exp(s_j)   (natural log, scale included).
+ * Prefill: query t sees keys 0..t (inclusive).  Decode: the query of
+ * sequence b stands at position seq_lens[b]-1 and sees keys
+ * 0..seq_lens[b]-1, so its own key and value must already be in the cache.
+ *
+ * Conventions for every entry point.
+ *  - Pointers marked "device" are device memory owned by the caller; the
+ *    library never allocates, frees, reads on the host or synchronises.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream)
+ *    and runs asynchronously; the call returns once it is enqueued.
+ *  - The return value is an attn_status_t.  Every argument check runs before
+ *    any HIP call, so a rejected call touches no device state.  A failed
+ *    launch returns ATTN_ERR_HIP; attn_last_error_message() describes the
+ *    most recent failure on the calling thread.
+ *  - Tensors are dense, row-major, in the layouts given below; 16-byte
+ *    aligned base pointers are required for q, k, v, out, the page pools and
+ *    the workspace, 4-byte alignment for lse, block_table and seq_lens.
+ */
+#ifndef ATTN_H
+#define ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum attn_status {
+    ATTN_OK = 0,
+    ATTN_ERR_INVALID_ARG = -1, /* null pointer, bad size, misaligned, Hq % Hkv != 0, ... */
+    ATTN_ERR_UNSUPPORTED = -2, /* valid request this build has no kernel for (dtype, d, page size) */
+    ATTN_ERR_WORKSPACE = -3,   /* workspace null or smaller than attn_decode_workspace_bytes() */
+    ATTN_ERR_HIP = -4          /* the HIP runtime reported an error while enqueuing */
+} attn_status_t;
+
+typedef enum attn_dtype {
+    ATTN_F32 = 0,  /* float32 q/k/v/out; fp32 arithmetic throughout */
+    ATTN_BF16 = 1  /* bfloat16 q/k/v/out; fp32 accumulation, bf16 MFMA products */
+} attn_dtype_t;
+
+/*
+ * Causal prefill (blockwise online softmax; see the file header).
+ *
+ *   q, out : device, [B, Hq,  T, d] in `dtype`
+ *   k, v   : device, [B, Hkv, T, d] in `dtype`
+ *   lse    : device, [B, Hq, T] float32, or NULL to skip it
+ *   B, T   : >= 0 (B == 0 or T == 0 enqueues nothing and returns ATTN_OK)
+ *   Hq,Hkv : >= 1, Hq % Hkv == 0
+ *   d      : 64 or 128
+ *   scale  : multiplies q.k (usually 1/sqrt(d)); any finite value
+ *   dtype  : ATTN_BF16 (d 64 or 128) or ATTN_F32 (d 64 or 128)
+ * out is written with round-to-nearest-even from the fp32 accumulator.
+ * q, k, v must hold finite values.
+ */
+int attn_prefill(const void* q, const void* k, const void* v, void* out, float* lse,
+                 int B, int Hq, int Hkv, int T, int d, float scale,
+                 attn_dtype_t dtype, hipStream_t stream);
+
+/*
+ * Split plan of attn_decode_paged: the number of splits S each sequence's
+ * page list is cut into (pages_per_split = ceil(max_pages_per_seq / S)).
+ * num_splits > 0 asks for that many (clamped to max_pages_per_seq);
+ * num_splits == 0 lets the library choose from the shape alone (no device
+ * query, no device read).  Returns S >= 1, or a negative attn_status_t for
+ * invalid sizes.
+ */
+int attn_decode_num_splits(int B, int Hq, int Hkv, int d, int page_size,
+                           int max_pages_per_seq, int num_splits);
+
+/*
+ * Bytes of device workspace attn_decode_paged needs for this shape and split
+ * request: fp32 partial outputs [B, Hq, S, d] and partial log-sum-exps
+ * [B, Hq, S], each region 256-byte aligned.  Returns 0 for invalid sizes.
+ */
+size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int d, int page_size,
+                                   int max_pages_per_seq, int num_splits);
+
+/*
+ * Single-token decode over a paged KV cache (split-KV + LSE combine).
+ *
+ *   q, out         : device, [B, Hq, d] in `dtype`
+ *   k_pages,v_pages: device, [num_pages, Hkv, page_size, d] in `dtype`; the
+ *                    (page, kv head) slice is contiguous (page_size*d values)
+ *   block_table    : device int32 [B, max_pages_per_seq]; token j of sequence
+ *                    b is slot j % page_size of page block_table[b][j / page_size].
+ *                    Entries past ceil(seq_lens[b] / page_size) are never read.
+ *   seq_lens       : device int32 [B]; cached tokens per sequence, each in
+ *                    [0, max_pages_per_seq * page_size].  0 gives out = 0 and
+ *                    lse = -inf for that sequence.
+ *   lse            : device float32 [B, Hq], or NULL to skip it
+ *   num_pages      : pool size; every block_table entry that is read must be
+ *                    in [0, num_pages)
+ *   num_splits     : as for attn_decode_num_splits (0 = automatic)
+ *   workspace      : device, at least attn_decode_workspace_bytes(...) bytes;
+ *                    owned by the caller, contents on entry are ignored
+ *   dtype          : ATTN_BF16; d = 128 or 64; page_size = 16
+ * Slots at or past seq_lens[b] may hold anything (NaN included): they are
+ * never used.  The block table and seq_lens are read on the device only;
+ * values outside the ranges above are undefined behaviour (check them with
+ * attn_validate_paged_metadata).  Calls that share a workspace must not
+ * overlap in time.
+ */
+int attn_decode_paged(const void* q, const void* k_pages, const void* v_pages,
+                      const int32_t* block_table, const int32_t* seq_lens,
+                      void* out, float* lse,
+                      int B, int Hq, int Hkv, int d, int page_size, int num_pages,
+                      int max_pages_per_seq, float scale, attn_dtype_t dtype,
+                      int num_splits, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream);
+
+/*
+ * Host-side check of paged metadata (host copies of block_table and
+ * seq_lens): every seq_len in [0, max_pages_per_seq * page_size] and every
+ * block-table entry that a sequence reads in [0, num_pages).  Returns ATTN_OK
+ * or ATTN_ERR_INVALID_ARG.  Touches no device.
+ */
+int attn_validate_paged_metadata(const int32_t* block_table_host, const int32_t* seq_lens_host,
+                                 int B, int max_pages_per_seq, int page_size, int num_pages);
+
+/* Static description of a status code (never NULL). */
+const char* attn_status_string(int status);
+
+/* Text describing the most recent failed call on this thread ("" if none). */
+const char* attn_last_error_message(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_H */

@@ -1,0 +1,164 @@
+"""C-ABI checks that need no GPU: the library loads, exports what the header
+declares, and rejects every invalid argument before touching HIP."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import attention_causal_gqa_amd as A
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return A.load_library()
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_header_declares_the_api():
+    names = declared_functions()
+    for n in ("attn_prefill", "attn_decode_paged", "attn_decode_workspace_bytes", "attn_decode_num_splits",
+              "attn_validate_paged_metadata", "attn_status_string", "attn_last_error_message"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+        # exported with C linkage (unmangled)
+        ctypes.CDLL(A.LIB_PATH)[name]
+
+
+def test_status_strings(lib):
+    for st in (A.ATTN_OK, A.ATTN_ERR_INVALID_ARG, A.ATTN_ERR_UNSUPPORTED, A.ATTN_ERR_WORKSPACE, A.ATTN_ERR_HIP, 7):
+        assert A.attn_status_string(st)
+
+
+FAKE = 1 << 20  # a 16-byte aligned non-null address; never dereferenced by rejected calls
+
+
+def prefill(lib, q=FAKE, k=FAKE, v=FAKE, out=FAKE, lse=None, B=1, Hq=4, Hkv=2, T=16, d=128, scale=0.1, dtype=1):
+    return lib.attn_prefill(q, k, v, out, lse, B, Hq, Hkv, T, d, scale, dtype, None)
+
+
+@pytest.mark.parametrize(
+    "kw,status",
+    [
+        (dict(q=None), A.ATTN_ERR_INVALID_ARG),
+        (dict(out=None), A.ATTN_ERR_INVALID_ARG),
+        (dict(q=FAKE + 8), A.ATTN_ERR_INVALID_ARG),
+        (dict(lse=FAKE + 2), A.ATTN_ERR_INVALID_ARG),
+        (dict(Hq=3, Hkv=2), A.ATTN_ERR_INVALID_ARG),
+        (dict(Hkv=0), A.ATTN_ERR_INVALID_ARG),
+        (dict(B=-1), A.ATTN_ERR_INVALID_ARG),
+        (dict(T=-5), A.ATTN_ERR_INVALID_ARG),
+        (dict(d=0), A.ATTN_ERR_INVALID_ARG),
+        (dict(scale=float("nan")), A.ATTN_ERR_INVALID_ARG),
+        (dict(scale=float("inf")), A.ATTN_ERR_INVALID_ARG),
+        (dict(dtype=7), A.ATTN_ERR_INVALID_ARG),
+        (dict(d=96), A.ATTN_ERR_UNSUPPORTED),
+        (dict(d=256, dtype=0), A.ATTN_ERR_UNSUPPORTED),
+        (dict(Hq=256, Hkv=1), A.ATTN_ERR_UNSUPPORTED),
+    ],
+)
+def test_prefill_rejects(lib, kw, status):
+    assert prefill(lib, **kw) == status
+    assert A.attn_last_error_message() != ""
+
+
+def test_prefill_empty_is_a_no_op(lib):
+    assert prefill(lib, q=None, k=None, v=None, out=None, B=0) == A.ATTN_OK
+    assert prefill(lib, q=None, k=None, v=None, out=None, T=0) == A.ATTN_OK
+
+
+def decode(lib, q=FAKE, kp=FAKE, vp=FAKE, bt=FAKE, sl=FAKE, out=FAKE, lse=None, B=2, Hq=4, Hkv=2, d=128, ps=16,
+           P=10, W=8, scale=0.1, dtype=1, ns=0, ws=FAKE, wsb=None):
+    if wsb is None:
+        wsb = lib.attn_decode_workspace_bytes(max(B, 0), Hq, Hkv, d, ps, W, ns) if B >= 0 else 0
+    return lib.attn_decode_paged(q, kp, vp, bt, sl, out, lse, B, Hq, Hkv, d, ps, P, W, scale, dtype, ns, ws, wsb,
+                                 None)
+
+
+@pytest.mark.parametrize(
+    "kw,status",
+    [
+        (dict(q=None), A.ATTN_ERR_INVALID_ARG),
+        (dict(bt=None), A.ATTN_ERR_INVALID_ARG),
+        (dict(sl=None), A.ATTN_ERR_INVALID_ARG),
+        (dict(kp=FAKE + 4), A.ATTN_ERR_INVALID_ARG),
+        (dict(bt=FAKE + 2), A.ATTN_ERR_INVALID_ARG),
+        (dict(Hq=5, Hkv=2), A.ATTN_ERR_INVALID_ARG),
+        (dict(B=-1), A.ATTN_ERR_INVALID_ARG),
+        (dict(W=0), A.ATTN_ERR_INVALID_ARG),
+        (dict(P=-1), A.ATTN_ERR_INVALID_ARG),
+        (dict(ns=-2), A.ATTN_ERR_INVALID_ARG),
+        (dict(scale=float("nan")), A.ATTN_ERR_INVALID_ARG),
+        (dict(ws=FAKE + 4), A.ATTN_ERR_INVALID_ARG),
+        (dict(dtype=0), A.ATTN_ERR_UNSUPPORTED),
+        (dict(d=80), A.ATTN_ERR_UNSUPPORTED),
+        (dict(ps=32), A.ATTN_ERR_UNSUPPORTED),
+        (dict(Hq=32, Hkv=2), A.ATTN_ERR_UNSUPPORTED),
+        (dict(ws=None), A.ATTN_ERR_WORKSPACE),
+        (dict(wsb=16), A.ATTN_ERR_WORKSPACE),
+    ],
+)
+def test_decode_rejects(lib, kw, status):
+    assert decode(lib, **kw) == status
+
+
+def test_decode_empty_batch_is_a_no_op(lib):
+    assert decode(lib, q=None, kp=None, vp=None, bt=None, sl=None, out=None, B=0, ws=None, wsb=0) == A.ATTN_OK
+
+
+def test_split_plan_and_workspace(lib):
+    # Explicit split counts: ceil(W / ceil(W / S)), clamped to W.
+    assert A.attn_decode_num_splits(4, 8, 4, 128, 16, 128, 1) == 1
+    assert A.attn_decode_num_splits(4, 8, 4, 128, 16, 128, 8) == 8
+    assert A.attn_decode_num_splits(4, 8, 4, 128, 16, 128, 3) == 3
+    assert A.attn_decode_num_splits(4, 8, 4, 128, 16, 5, 100) == 5
+    # Automatic plans for the two paged workloads of the benchmark.
+    s4 = A.attn_decode_num_splits(32, 16, 8, 128, 16, 128, 0)
+    s5 = A.attn_decode_num_splits(64, 32, 8, 128, 16, 512, 0)
+    assert 32 * 8 * s4 >= 4096 and 64 * 8 * s5 >= 4096
+    for (B, Hq, Hkv, W, ns) in ((32, 16, 8, 128, 0), (64, 32, 8, 512, 0), (3, 6, 2, 9, 2)):
+        S = A.attn_decode_num_splits(B, Hq, Hkv, 128, 16, W, ns)
+        need = A.attn_decode_workspace_bytes(B, Hq, Hkv, 128, 16, W, ns)
+        assert need >= B * Hq * S * (128 + 1) * 4
+        assert need % 256 == 0
+    assert A.attn_decode_workspace_bytes(1, 3, 2, 128, 16, 4, 0) == 0  # invalid -> 0
+    with pytest.raises(A.AttnError):
+        A.attn_decode_num_splits(1, 4, 2, 96, 16, 4, 0)
+
+
+def test_validate_paged_metadata():
+    bt = np.array([[3, 1, -1], [0, -1, -1]], dtype=np.int32)
+    A.attn_validate_paged_metadata(bt, np.array([20, 16], dtype=np.int32), 16, 4)
+    A.attn_validate_paged_metadata(bt, np.array([0, 0], dtype=np.int32), 16, 4)
+    with pytest.raises(A.AttnError):
+        A.attn_validate_paged_metadata(bt, np.array([33, 1], dtype=np.int32), 16, 4)  # reads entry -1
+    with pytest.raises(A.AttnError):
+        A.attn_validate_paged_metadata(bt, np.array([49, 1], dtype=np.int32), 16, 4)  # past W * page_size
+    with pytest.raises(A.AttnError):
+        A.attn_validate_paged_metadata(bt, np.array([20, 1], dtype=np.int32), 16, 3)  # page 3 outside pool
+    with pytest.raises(A.AttnError):
+        A.attn_validate_paged_metadata(bt, np.array([-1, 1], dtype=np.int32), 16, 4)
+
+
+def test_product_path_has_no_cpu_fallback():
+    """The package never imports the oracle and has no compute of its own."""
+    pkg = os.path.join(ROOT, "attention_causal_gqa_amd")
+    for name in os.listdir(pkg):
+        if name.endswith(".py"):
+            src = open(os.path.join(pkg, name)).read()
+            assert not re.search(r"^\s*(import|from)\s+(\.\.)?oracle\b", src, flags=re.M), name
+            assert "import_module" not in src and "__import__" not in src, name

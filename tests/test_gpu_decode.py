@@ -1,0 +1,167 @@
+"""GPU parity of attn_decode_paged against the fp64 oracle (called through the C ABI)."""
+
+import numpy as np
+import pytest
+import torch
+
+import attention_causal_gqa_amd as A
+import oracle
+from attention_causal_gqa_amd import synth
+from tests._gpu import TOL_BF16, TOL_LSE, device, max_err, np64, say
+
+pytestmark = pytest.mark.gpu
+
+
+def to_dev(inp):
+    dev = device()
+    return (inp.q.to(dev), inp.k_pages.to(dev), inp.v_pages.to(dev), inp.block_table.to(dev), inp.seq_lens.to(dev))
+
+
+def run_decode(inp, scale, num_splits=0):
+    q, kp, vp, bt, sl = to_dev(inp)
+    out, lse = A.attn_decode_paged(q, kp, vp, bt, sl, scale=scale, num_splits=num_splits)
+    torch.cuda.synchronize()
+    return out.cpu(), lse.cpu()
+
+
+def oracle_decode(inp, scale, batches=None):
+    """Oracle over the chosen sequences (all by default); inputs upcast exactly."""
+    batches = list(range(inp.q.shape[0])) if batches is None else batches
+    idx = torch.tensor(batches, dtype=torch.long)
+    return oracle.decode_paged(np64(inp.q[idx]), inp.k_pages.float().numpy(), inp.v_pages.float().numpy(),
+                               inp.block_table[idx].numpy(), inp.seq_lens[idx].numpy(), scale, inp.page_size)
+
+
+def check(inp, scale, what, num_splits=0, batches=None):
+    A.attn_validate_paged_metadata(inp.block_table, inp.seq_lens, inp.page_size, inp.k_pages.shape[0])
+    say(f"[decode] {what}: B={inp.q.shape[0]} Hq={inp.q.shape[1]} pool={tuple(inp.k_pages.shape)} "
+        f"W={inp.max_pages_per_seq} splits={num_splits}")
+    out, lse = run_decode(inp, scale, num_splits)
+    ref_out, ref_lse = oracle_decode(inp, scale, batches)
+    sel = slice(None) if batches is None else torch.tensor(batches, dtype=torch.long)
+    e_o = max_err(np64(out[sel]), ref_out, f"{what} out", TOL_BF16)
+    e_l = max_err(np64(lse[sel]), ref_lse, f"{what} lse", TOL_LSE)
+    say(f"    max err out {e_o:.3e} lse {e_l:.3e}")
+    return out, lse
+
+
+# ------------------------------------------------------------------ workload 4, whole output
+def test_workload4_full():
+    shp = synth.WORKLOADS[4]["decode"]
+    inp = synth.paged_inputs(shp, seed=104, poison=float("nan"))
+    check(inp, synth.fp32_scale(shp.d), "workload 4 (B32 Hq16 Hkv8, L~U[32,2048], NaN-poisoned tails)")
+
+
+def test_workload5_decode_sampled():
+    shp = synth.WORKLOADS[5]["decode"]
+    inp = synth.paged_inputs(shp, seed=105)
+    rng = np.random.default_rng(105)
+    L = inp.seq_lens.numpy()
+    batches = sorted(set([int(np.argmin(L)), int(np.argmax(L))] + [int(x) for x in rng.integers(0, shp.B, 6)]))
+    out, lse = check(inp, synth.fp32_scale(shp.d), "workload 5 decode (B64 Hq32 Hkv8, L~U[1024,8192])",
+                     batches=batches)
+    assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
+
+
+# ------------------------------------------------------------------ lengths at page and split edges
+EDGE_LENS = [1, 2, 15, 16, 17, 31, 32, 33, 63, 64, 65, 255, 256, 257, 1000, 2047, 2048]
+
+
+@pytest.mark.parametrize("num_splits", [0, 1, 3])
+def test_edge_lengths(num_splits):
+    shp = synth.DecodeShape(len(EDGE_LENS), 8, 4, 128, 16, 1, 2048, torch.bfloat16)
+    inp = synth.paged_inputs(shp, seed=7, seq_lens=EDGE_LENS, extra_pages=5, poison=float("nan"))
+    check(inp, synth.fp32_scale(128), f"edge lengths, splits={num_splits}", num_splits=num_splits)
+
+
+@pytest.mark.parametrize("Hq,Hkv,d", [(8, 8, 128), (6, 2, 128), (7, 1, 128), (16, 2, 128), (8, 2, 64), (4, 4, 64)])
+def test_group_sizes_and_d(Hq, Hkv, d):
+    shp = synth.DecodeShape(5, Hq, Hkv, d, 16, 1, 700, torch.bfloat16)
+    inp = synth.paged_inputs(shp, seed=Hq * 10 + Hkv + d, poison=float("nan"))
+    check(inp, synth.fp32_scale(d), f"Hq{Hq} Hkv{Hkv} d{d}")
+
+
+def test_empty_sequence():
+    shp = synth.DecodeShape(4, 4, 2, 128, 16, 1, 300, torch.bfloat16)
+    inp = synth.paged_inputs(shp, seed=11, seq_lens=[0, 5, 0, 300], poison=float("nan"))
+    out, lse = check(inp, synth.fp32_scale(128), "seq_len 0 rows")
+    assert torch.all(out[[0, 2]].float() == 0) and torch.all(torch.isneginf(lse[[0, 2]]))
+
+
+def test_zero_query_is_mean_of_cached_values():
+    shp = synth.DecodeShape(6, 8, 2, 128, 16, 1, 900, torch.bfloat16)
+    inp = synth.paged_inputs(shp, seed=12, poison=float("nan"))
+    inp.q.zero_()
+    say("[decode] q = 0 closed form")
+    out, lse = run_decode(inp, synth.fp32_scale(128))
+    for b in range(6):
+        L = int(inp.seq_lens[b])
+        for h in range(8):
+            vals = oracle.gather_pages(inp.v_pages.float().numpy(), inp.block_table[b].numpy(), L, 16, h // 4)
+            max_err(np64(out[b, h]), vals.mean(axis=0), f"q=0 b{b} h{h}", TOL_BF16)
+        max_err(np64(lse[b]), np.full(8, np.log(L)), f"q=0 lse b{b}", TOL_LSE)
+
+
+# ------------------------------------------------------------------ invariants on the GPU
+def test_page_permutation_is_bit_identical():
+    shp = synth.DecodeShape(9, 8, 2, 128, 16, 1, 1500, torch.bfloat16)
+    inp = synth.paged_inputs(shp, seed=13, extra_pages=7, poison=float("nan"))
+    k2, v2, t2 = synth.permute_pages(inp.k_pages, inp.v_pages, inp.block_table, seed=14)
+    inp2 = synth.PagedInputs(inp.q, k2, v2, t2, inp.seq_lens, 16)
+    assert not torch.equal(t2, inp.block_table)
+    say("[decode] page permutation")
+    for ns in (0, 2):
+        o1, l1 = run_decode(inp, synth.fp32_scale(128), ns)
+        o2, l2 = run_decode(inp2, synth.fp32_scale(128), ns)
+        assert torch.equal(o1, o2) and torch.equal(l1, l2), f"splits={ns}"
+
+
+def test_split_count_invariance():
+    shp = synth.DecodeShape(8, 8, 4, 128, 16, 500, 2048, torch.bfloat16)
+    inp = synth.paged_inputs(shp, seed=15)
+    ref_out, ref_lse = oracle_decode(inp, synth.fp32_scale(128))
+    say("[decode] split invariance")
+    outs = {}
+    for ns in (1, 2, 5, 16, 128, 0):
+        o, l = run_decode(inp, synth.fp32_scale(128), ns)
+        max_err(np64(o), ref_out, f"splits={ns} out", TOL_BF16)
+        max_err(np64(l), ref_lse, f"splits={ns} lse", TOL_LSE)
+        outs[ns] = o
+    max_err(np64(outs[1]), np64(outs[0]), "splits 1 vs auto", TOL_BF16)
+
+
+def test_decode_equals_prefill_row():
+    """Decode with L = t + 1 cached tokens equals prefill row t (each within tolerance of the oracle and of each other)."""
+    shp = synth.PrefillShape(2, 8, 2, 320, 128, torch.bfloat16)
+    q, k, v = synth.prefill_inputs(shp, seed=16)
+    dev = device()
+    say("[decode] decode(t) == prefill row t")
+    pout, plse = A.attn_prefill(q.to(dev), k.to(dev), v.to(dev), scale=synth.fp32_scale(128))
+    torch.cuda.synchronize()
+    pout, plse = pout.cpu(), plse.cpu()
+    ts = [0, 1, 15, 16, 17, 100, 255, 256, 319]
+    for t in ts:
+        kp, vp, bt, sl = synth.paged_from_dense(k, v, [t + 1, t + 1], 16, seed=t, W=20)
+        inp = synth.PagedInputs(q[:, :, t].contiguous(), kp, vp, bt, sl, 16)
+        dout, dlse = run_decode(inp, synth.fp32_scale(128))
+        max_err(np64(dout), np64(pout[:, :, t]), f"decode vs prefill row {t} out", TOL_BF16)
+        max_err(np64(dlse), np64(plse[:, :, t]), f"decode vs prefill row {t} lse", TOL_LSE)
+        ro, rl = oracle.prefill_rows(q.float().numpy(), k.float().numpy(), v.float().numpy(),
+                                     synth.fp32_scale(128), 1, 5, [t])
+        max_err(np64(dout[1, 5])[None], ro, f"decode row {t} vs oracle", TOL_BF16)
+
+
+def test_workspace_reuse_and_explicit_workspace():
+    shp = synth.DecodeShape(3, 4, 2, 128, 16, 1, 400, torch.bfloat16)
+    inp = synth.paged_inputs(shp, seed=17)
+    q, kp, vp, bt, sl = to_dev(inp)
+    need = A.attn_decode_workspace_bytes(3, 4, 2, 128, 16, inp.max_pages_per_seq, 0)
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device=q.device)  # garbage contents
+    say("[decode] caller workspace")
+    o1, l1 = A.attn_decode_paged(q, kp, vp, bt, sl, workspace=ws)
+    o2, l2 = A.attn_decode_paged(q, kp, vp, bt, sl, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    with pytest.raises(A.AttnError) as ei:
+        A.attn_decode_paged(q, kp, vp, bt, sl, workspace=ws[: need - 256])
+    assert ei.value.status == A.ATTN_ERR_WORKSPACE

@@ -1,0 +1,182 @@
+"""GPU parity of attn_prefill against the fp64 oracle (called through the C ABI)."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import attention_causal_gqa_amd as A
+import oracle
+from attention_causal_gqa_amd import synth
+from tests._gpu import TOL_BF16, TOL_F32, TOL_LSE, device, max_err, np64, say
+
+pytestmark = pytest.mark.gpu
+
+
+def run_prefill(q, k, v, scale):
+    dev = device()
+    out, lse = A.attn_prefill(q.to(dev), k.to(dev), v.to(dev), scale=scale)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def check_full(q, k, v, scale, tol, what):
+    say(f"[prefill] {what}: q{tuple(q.shape)} k{tuple(k.shape)} {q.dtype} scale={scale}")
+    out, lse = run_prefill(q, k, v, scale)
+    ref_out, ref_lse = oracle.prefill(np64(q), np64(k), np64(v), scale)
+    e_out = max_err(np64(out), ref_out, f"{what} out", tol)
+    e_lse = max_err(np64(lse), ref_lse, f"{what} lse", TOL_LSE)
+    say(f"    max err out {e_out:.3e} lse {e_lse:.3e}")
+    return out, lse
+
+
+# ------------------------------------------------------------------ workloads 1 and 2, whole output
+def test_workload1_fp32_mha():
+    shp = synth.WORKLOADS[1]["prefill"]
+    q, k, v = synth.prefill_inputs(shp, seed=1)
+    check_full(q, k, v, synth.fp32_scale(shp.d), TOL_F32, "workload 1 (fp32 MHA T128 d64)")
+
+
+def test_workload2_bf16_gqa():
+    shp = synth.WORKLOADS[2]["prefill"]
+    q, k, v = synth.prefill_inputs(shp, seed=2)
+    check_full(q, k, v, synth.fp32_scale(shp.d), TOL_BF16, "workload 2 (bf16 GQA T512 d128)")
+
+
+# ------------------------------------------------------------------ shapes: ragged T, every group size, d 64/128
+BF16_SHAPES = [
+    # B, Hq, Hkv, T, d
+    (1, 1, 1, 1, 128),
+    (2, 4, 2, 7, 128),
+    (1, 8, 2, 63, 128),
+    (1, 4, 1, 65, 128),
+    (2, 6, 2, 200, 128),   # g = 3: 42 tokens x 3 heads per workgroup, two dead rows
+    (1, 16, 2, 257, 128),  # g = 8
+    (1, 3, 3, 100, 128),   # MHA
+    (1, 32, 1, 40, 128),   # g = 32: 4 tokens per workgroup
+    (1, 7, 1, 90, 128),    # g = 7
+    (1, 8, 1, 130, 64),
+    (2, 2, 2, 129, 64),
+    (1, 12, 4, 300, 64),
+]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,T,d", BF16_SHAPES)
+def test_bf16_shapes(B, Hq, Hkv, T, d):
+    shp = synth.PrefillShape(B, Hq, Hkv, T, d, torch.bfloat16)
+    q, k, v = synth.prefill_inputs(shp, seed=1000 + T + Hq)
+    check_full(q, k, v, synth.fp32_scale(d), TOL_BF16, f"bf16 B{B} Hq{Hq} Hkv{Hkv} T{T} d{d}")
+
+
+F32_SHAPES = [(1, 1, 1, 1, 64), (2, 4, 2, 100, 64), (1, 2, 2, 200, 128), (1, 6, 3, 129, 128)]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,T,d", F32_SHAPES)
+def test_f32_shapes(B, Hq, Hkv, T, d):
+    shp = synth.PrefillShape(B, Hq, Hkv, T, d, torch.float32)
+    q, k, v = synth.prefill_inputs(shp, seed=2000 + T)
+    check_full(q, k, v, synth.fp32_scale(d), TOL_F32, f"fp32 B{B} Hq{Hq} Hkv{Hkv} T{T} d{d}")
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.125, 0.5, 1e-3])
+def test_bf16_scale_values(scale):
+    shp = synth.PrefillShape(1, 4, 2, 150, 128, torch.bfloat16)
+    q, k, v = synth.prefill_inputs(shp, seed=77)
+    check_full(q, k, v, float(np.float32(scale)), TOL_BF16, f"bf16 scale {scale}")
+
+
+@pytest.mark.parametrize("dtype,tol", [(torch.bfloat16, TOL_BF16), (torch.float32, TOL_F32)])
+def test_zero_query_is_prefix_mean(dtype, tol):
+    """q = 0: out_i = mean_{j<=i} v_j of the kv head h // g, lse_i = ln(i + 1)."""
+    shp = synth.PrefillShape(2, 8, 2, 200, 128, dtype)
+    _, k, v = synth.prefill_inputs(shp, seed=5)
+    v[:, 1] += 3.0  # distinct values per kv head
+    q = torch.zeros(2, 8, 200, 128, dtype=dtype)
+    say(f"[prefill] q = 0 closed form {dtype}")
+    out, lse = run_prefill(q, k, v, synth.fp32_scale(128))
+    vv = np64(v)
+    mean = np.cumsum(vv, axis=2) / np.arange(1, 201)[None, None, :, None]
+    want = np.repeat(mean, 4, axis=1)
+    max_err(np64(out), want, "q=0 out", tol)
+    max_err(np64(lse), np.broadcast_to(np.log(np.arange(1, 201)), (2, 8, 200)), "q=0 lse", TOL_LSE)
+
+
+def test_single_token_returns_v_exactly():
+    shp = synth.PrefillShape(3, 8, 4, 1, 128, torch.bfloat16)
+    q, k, v = synth.prefill_inputs(shp, seed=6)
+    say("[prefill] T = 1")
+    out, lse = run_prefill(q, k, v, synth.fp32_scale(128))
+    assert torch.equal(out.cpu(), v.repeat_interleave(2, dim=1)), "T=1 must return v_0 bit for bit"
+    dots = (np64(q) * np.repeat(np64(k), 2, axis=1)).sum(-1)
+    max_err(np64(lse), synth.fp32_scale(128) * dots, "T=1 lse", TOL_LSE)
+
+
+def test_row_zero_is_v0_for_long_rows():
+    """Row 0 sees only key 0: out is v_0 exactly, whatever T is."""
+    shp = synth.PrefillShape(1, 8, 2, 700, 128, torch.bfloat16)
+    q, k, v = synth.prefill_inputs(shp, seed=8)
+    say("[prefill] row 0 == v_0")
+    out, _ = run_prefill(q, k, v, synth.fp32_scale(128))
+    assert torch.equal(out[:, :, 0].cpu(), v[:, :, 0].repeat_interleave(4, dim=1))
+
+
+def test_causality_future_keys_do_not_leak():
+    shp = synth.PrefillShape(1, 4, 2, 300, 128, torch.bfloat16)
+    q, k, v = synth.prefill_inputs(shp, seed=9)
+    say("[prefill] causality")
+    out1, lse1 = run_prefill(q, k, v, synth.fp32_scale(128))
+    k2, v2 = k.clone(), v.clone()
+    k2[:, :, 171:] = 7.0
+    v2[:, :, 171:] = -9.0
+    out2, lse2 = run_prefill(q, k2, v2, synth.fp32_scale(128))
+    assert torch.equal(out1[:, :, :171].cpu(), out2[:, :, :171].cpu())
+    assert torch.equal(lse1[:, :, :171].cpu(), lse2[:, :, :171].cpu())
+
+
+def test_lse_is_optional_and_out_is_identical():
+    shp = synth.PrefillShape(1, 4, 2, 97, 128, torch.bfloat16)
+    q, k, v = synth.prefill_inputs(shp, seed=10)
+    dev = device()
+    say("[prefill] lse = NULL")
+    o1, _ = A.attn_prefill(q.to(dev), k.to(dev), v.to(dev))
+    o2, l2 = A.attn_prefill(q.to(dev), k.to(dev), v.to(dev), lse=False)
+    torch.cuda.synchronize()
+    assert l2 is None and torch.equal(o1.cpu(), o2.cpu())
+
+
+# ------------------------------------------------------------------ full-size workloads, sampled rows
+def sampled_rows(T, rng, n=24):
+    fixed = [0, 1, 63, 64, 65, 127, 128, T // 2, T - 65, T - 64, T - 2, T - 1]
+    rows = set(x for x in fixed if 0 <= x < T)
+    rows.update(int(x) for x in rng.integers(0, T, n))
+    return sorted(rows)
+
+
+@pytest.mark.parametrize("workload", [3, 5])
+def test_full_size_prefill_sampled(workload):
+    shp = synth.WORKLOADS[workload]["prefill"]
+    q, k, v = synth.prefill_inputs(shp, seed=workload)
+    scale = synth.fp32_scale(shp.d)
+    say(f"[prefill] workload {workload} full size {shp}")
+    out, lse = run_prefill(q, k, v, scale)
+    out, lse = out.cpu(), lse.cpu()
+    qn, kn, vn = q.float().numpy(), k.float().numpy(), v.float().numpy()  # exact upcast for the oracle
+    rng = np.random.default_rng(workload)
+    heads = sorted(set([0, shp.Hq - 1] + [int(x) for x in rng.integers(0, shp.Hq, 3)]))
+    worst = 0.0
+    for b in range(shp.B):
+        for h in heads:
+            rows = sampled_rows(shp.T, rng)
+            ro, rl = oracle.prefill_rows(qn, kn, vn, scale, b, h, rows)
+            worst = max(worst, max_err(np64(out[b, h, rows]), ro, f"w{workload} b{b} h{h} out", TOL_BF16))
+            max_err(np64(lse[b, h, rows]), rl, f"w{workload} b{b} h{h} lse", TOL_LSE)
+    say(f"    sampled max err {worst:.3e}")
+    # Properties at every position: finite; out is a convex combination of
+    # the kv head's values (|out| <= max |v|, up to one bf16 rounding); and
+    # lse_t >= s_t0, the score of key 0, which every row sees.
+    assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
+    vmax = v.float().abs().amax(dim=(2, 3)).repeat_interleave(shp.Hq // shp.Hkv, dim=1)
+    assert (out.float().abs().amax(dim=(2, 3)) <= vmax * (1 + 2.0**-8)).all()
+    s0 = scale * (q.float() * k.float()[:, :, :1].repeat_interleave(shp.Hq // shp.Hkv, dim=1)).sum(-1)
+    assert (lse >= s0 - 1e-3).all()
