@@ -1,0 +1,248 @@
+"""Benchmark of the attention hot path on one MI355X.
+
+One step = one pass of the whole path over the mixed long-context workload:
+causal GQA prefill (B1 Hq32 Hkv8 T8192 d128, bf16) followed by paged
+single-token decode (B64 Hq32 Hkv8 d128, page 16, seq_lens ~ U[1024, 8192]),
+i.e. the prefill kernel, the split-KV decode kernel and the LSE combine
+kernel.  Inputs are seeded synthetic tensors, resident in HBM before timing.
+
+Prints one JSON line.  ``value`` is the step's roofline fraction: the time the
+step's algorithmic work takes at MI355X peak (prefill flops at the bf16 MFMA
+peak plus decode bytes at the HBM peak) divided by the measured step time.
+Per-kernel rates come from HIP events recorded on the launch stream.
+
+    python bench.py [--steps K] [--warmup W] [--workload 5|3|4] [--no-cpu-baseline]
+"""
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import attention_causal_gqa_amd as A  # noqa: E402
+from attention_causal_gqa_amd import synth  # noqa: E402
+
+PEAK_BF16_FLOPS = 2.5e15  # MI355X dense bf16 MFMA, published
+PEAK_HBM_BYTES = 8.0e12   # MI355X HBM3E, published
+METRIC = "prefill TFLOP/s and paged-decode HBM GB/s, as fraction of MI355X peak"
+PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", type=int, default=5, choices=(3, 4, 5))
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--flush", action="store_true",
+                   help="write a 512 MiB buffer before each step (outside the kernel events) to evict L2/MALL")
+    return p.parse_args()
+
+
+def kernel_source_hash(names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "attention_causal_gqa_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel, src_hash):
+    """HBM bytes per launch from the committed rocprofv3 --pmc summary, if it was taken on this source."""
+    if not os.path.exists(PROFILE_COUNTERS):
+        return None
+    for line in open(PROFILE_COUNTERS):
+        parts = line.split()
+        if len(parts) == 4 and parts[0] == "traffic" and parts[1] == kernel and parts[2] == src_hash:
+            return int(parts[3])
+    return None
+
+
+def cpu_baseline(pre_inputs, pre_shape, dec_inputs, budget_s=20.0):
+    """Time the fp64 oracle, as it stands, on a bounded sample of the same workload."""
+    import oracle
+    from threadpoolctl import threadpool_info
+
+    threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    q, k, v = pre_inputs
+    qn, kn, vn = (t.float().numpy() for t in (q, k, v))
+    scale = synth.fp32_scale(pre_shape.d)
+    g = pre_shape.Hq // pre_shape.Hkv
+    t0 = time.perf_counter()
+    heads = 0
+    flops = 0
+    # prefill, one query head at a time (with its kv head), until half the budget is used
+    while heads < pre_shape.Hq and (heads == 0 or time.perf_counter() - t0 < budget_s / 2):
+        h = heads
+        oracle.prefill(qn[:, h:h + 1], kn[:, h // g:h // g + 1], vn[:, h // g:h // g + 1], scale)
+        flops += 2 * pre_shape.B * pre_shape.d * pre_shape.T * (pre_shape.T + 1)
+        heads += 1
+    t_pre = time.perf_counter() - t0
+    seqs = 0
+    dbytes = 0
+    t1 = time.perf_counter()
+    kp, vp = dec_inputs.k_pages.float().numpy(), dec_inputs.v_pages.float().numpy()
+    t_conv = time.perf_counter() - t1
+    t1 = time.perf_counter()
+    B, Hq, d = dec_inputs.q.shape
+    Hkv = dec_inputs.k_pages.shape[1]
+    while seqs < B and (seqs == 0 or time.perf_counter() - t1 < budget_s / 2):
+        b = seqs
+        oracle.decode_paged(dec_inputs.q[b:b + 1].float().numpy(), kp, vp, dec_inputs.block_table[b:b + 1].numpy(),
+                            dec_inputs.seq_lens[b:b + 1].numpy(), scale, dec_inputs.page_size)
+        L = int(dec_inputs.seq_lens[b])
+        dbytes += 2 * L * Hkv * d * 2 + 2 * Hq * d * 2 + 4 * (-(-L // 16)) + 4
+        seqs += 1
+    t_dec = time.perf_counter() - t1
+    frac = (flops / PEAK_BF16_FLOPS + dbytes / PEAK_HBM_BYTES) / (t_pre + t_dec)
+    return {
+        "value": frac,
+        "unit": "fraction of MI355X roofline",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (f"fp64 oracle: prefill of {heads} of {pre_shape.Hq} query heads at T={pre_shape.T} "
+                   f"({t_pre:.2f} s) + paged decode of {seqs} of {B} sequences, all {Hq} heads ({t_dec:.2f} s); "
+                   f"same seeded inputs"),
+        "prefill_tflops": flops / t_pre / 1e12,
+        "decode_gbps": dbytes / t_dec / 1e9,
+        "host_cpu_count": os.cpu_count(),
+        "pool_upcast_s": round(t_conv, 2),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on one GPU only: the attention path has no multi-GPU "
+                                   "code; run without --gpus or with --gpus 1"}))
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    A.load_library()
+    wl = synth.WORKLOADS[args.workload]
+    pre_shape = wl.get("prefill")
+    dec_shape = wl.get("decode")
+
+    pre_inputs = dec_inputs = None
+    work = {}
+    if pre_shape is not None:
+        pre_inputs = synth.prefill_inputs(pre_shape, seed=args.workload)
+        q, k, v = (t.to(dev) for t in pre_inputs)
+        out = torch.empty_like(q)
+        lse = torch.empty(pre_shape.B, pre_shape.Hq, pre_shape.T, dtype=torch.float32, device=dev)
+        scale = synth.fp32_scale(pre_shape.d)
+        work["prefill"] = lambda: A.attn_prefill(q, k, v, out=out, lse=lse, scale=scale)
+    if dec_shape is not None:
+        dec_inputs = synth.paged_inputs(dec_shape, seed=100 + args.workload)
+        dq, kp, vp, bt, sl = (t.to(dev) for t in (dec_inputs.q, dec_inputs.k_pages, dec_inputs.v_pages,
+                                                  dec_inputs.block_table, dec_inputs.seq_lens))
+        dout = torch.empty_like(dq)
+        dlse = torch.empty(dq.shape[0], dq.shape[1], dtype=torch.float32, device=dev)
+        W = dec_inputs.max_pages_per_seq
+        need = A.attn_decode_workspace_bytes(dec_shape.B, dec_shape.Hq, dec_shape.Hkv, dec_shape.d,
+                                             dec_shape.page_size, W, 0)
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+        dscale = synth.fp32_scale(dec_shape.d)
+        work["decode"] = lambda: A.attn_decode_paged(dq, kp, vp, bt, sl, out=dout, lse=dlse, scale=dscale,
+                                                     workspace=ws)
+    flush_buf = torch.empty(512 << 20, dtype=torch.uint8, device=dev) if args.flush else None
+
+    names = list(work)
+    stream = torch.cuda.current_stream()
+
+    def step(events=None):
+        if flush_buf is not None:
+            flush_buf.fill_(1)
+        for i, n in enumerate(names):
+            if events is not None:
+                events[i].record(stream)
+            work[n]()
+        if events is not None:
+            events[len(names)].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(evs[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    per = {n: [evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(args.steps)] for i, n in enumerate(names)}
+    ms = {n: float(np.mean(per[n])) for n in names}
+    kernel_ms = sum(ms.values())
+    ms_per_step = wall * 1e3 / args.steps
+
+    result = {"metric": METRIC}
+    at_peak = 0.0
+    parts = {}
+    if pre_shape is not None:
+        flops = pre_shape.flops()
+        t = ms["prefill"] / 1e3
+        at_peak += flops / PEAK_BF16_FLOPS
+        parts["prefill"] = {"ms": round(ms["prefill"], 4), "ms_min": round(min(per["prefill"]), 4),
+                            "tflops": round(flops / t / 1e12, 1), "frac_of_peak": round(flops / t / PEAK_BF16_FLOPS, 4),
+                            "flops_per_launch": flops}
+    if dec_shape is not None:
+        nbytes = dec_inputs.algorithmic_bytes()
+        t = ms["decode"] / 1e3
+        at_peak += nbytes / PEAK_HBM_BYTES
+        parts["decode"] = {"ms": round(ms["decode"], 4), "ms_min": round(min(per["decode"]), 4),
+                           "gbps": round(nbytes / t / 1e9, 1), "frac_of_peak": round(nbytes / t / PEAK_HBM_BYTES, 4),
+                           "bytes_per_launch": nbytes, "kernels": "split + combine",
+                           "num_splits": A.attn_decode_num_splits(dec_shape.B, dec_shape.Hq, dec_shape.Hkv,
+                                                                  dec_shape.d, dec_shape.page_size,
+                                                                  dec_inputs.max_pages_per_seq, 0)}
+    value = at_peak / (ms_per_step / 1e3)
+
+    # Dominant kernel's roofline (the one with the larger share of the step).
+    dom = max(names, key=lambda n: ms[n])
+    if dom == "prefill":
+        src = kernel_source_hash(["prefill_bf16.hip", "device_common.h"])
+        roof = {"kernel": "prefill_bf16_kernel", "bound": "mfma", "achieved": parts["prefill"]["tflops"],
+                "peak": PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s",
+                "frac": round(parts["prefill"]["tflops"] * 1e12 / PEAK_BF16_FLOPS, 4),
+                "traffic": measured_traffic("prefill_bf16_kernel", src), "source_hash": src}
+    else:
+        src = kernel_source_hash(["decode_paged.hip", "device_common.h"])
+        roof = {"kernel": "decode_split_kernel+decode_combine_kernel", "bound": "hbm",
+                "achieved": parts["decode"]["gbps"], "peak": PEAK_HBM_BYTES / 1e9, "unit": "GB/s",
+                "frac": round(parts["decode"]["gbps"] * 1e9 / PEAK_HBM_BYTES, 4),
+                "traffic": measured_traffic("decode_split_kernel", src), "source_hash": src}
+
+    cfg = {"workload": synth.WORKLOAD_NAMES[args.workload], "seed_prefill": args.workload,
+           "seed_decode": 100 + args.workload}
+    if dec_inputs is not None:
+        cfg["decode_tokens"] = int(dec_inputs.seq_lens.sum())
+    result.update({
+        "value": round(value, 4),
+        "unit": "fraction of MI355X roofline (step time at peak / measured step time)",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "kernel_ms_per_step": round(kernel_ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": cfg,
+        "parts": parts,
+        "roofline": roof,
+    })
+    if not args.no_cpu_baseline and args.workload == 5:
+        result["cpu_baseline"] = cpu_baseline(pre_inputs, pre_shape, dec_inputs)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
