@@ -31,6 +31,8 @@ FLAGS = [
     "-munsafe-fp-atomics",
     # No packed fp32 (v_pk_fma/mul/add_f32) in device code.
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # Keep register arrays in registers: the LDS budget belongs to the K/V tiles.
+    "-mllvm", "-disable-promote-alloca-to-lds=true",
     "-I", os.path.join(ROOT, "include"),
     "-I", CSRC,
 ]
@@ -41,6 +43,19 @@ def hipcc():
         if cand and os.path.exists(cand):
             return cand
     raise RuntimeError("hipcc not found (set ROCM_PATH)")
+
+
+def _scratch_users(remarks):
+    """Kernels the compiler gave private scratch memory (stack arrays or spills)."""
+    users, name = [], None
+    for line in remarks.splitlines():
+        if "Function Name:" in line:
+            name = line.split("Function Name:")[1].split()[0]
+        elif "ScratchSize [bytes/lane]:" in line:
+            n = int(line.split("ScratchSize [bytes/lane]:")[1].split()[0])
+            if n:
+                users.append(f"{name} ({n} B/lane)")
+    return users
 
 
 def _run(cmd):
@@ -56,16 +71,23 @@ def build(verbose=False):
     jobs = []
     for src in SOURCES:
         obj = os.path.join(BUILD, src.rsplit(".", 1)[0] + ".o")
-        jobs.append((src, obj, [cc, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]))
+        jobs.append((src, obj, [cc, *FLAGS, "-Rpass-analysis=kernel-resource-usage", "-c", os.path.join(CSRC, src),
+                                "-o", obj]))
     workers = min(len(jobs), max(1, min(8, os.cpu_count() or 1)))
     with concurrent.futures.ThreadPoolExecutor(workers) as ex:
         results = list(ex.map(lambda j: (j[0], *_run(j[2])), jobs))
     failed = [(s, out) for s, rc, out in results if rc != 0]
     for s, rc, out in results:
-        if out.strip() and (verbose or rc != 0):
-            print(f"--- {s}\n{out}", file=sys.stderr)
+        text = "\n".join(l for l in out.splitlines() if "kernel-resource-usage" not in l)
+        if text.strip() and (verbose or rc != 0):
+            print(f"--- {s}\n{text}", file=sys.stderr)
     if failed:
         raise RuntimeError("hipcc failed for: " + ", ".join(s for s, _ in failed))
+    # Every hot loop must live in registers and LDS: scratch means a stack
+    # array the compiler could not promote, or a spill.
+    scratch = [u for _, _, out in results for u in _scratch_users(out)]
+    if scratch:
+        raise RuntimeError("kernels use scratch memory: " + "; ".join(scratch))
     tmp = LIB + ".tmp"
     rc, out = _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *[j[1] for j in jobs], "-o", tmp])
     if rc != 0:

@@ -11,7 +11,7 @@
 #include <cstdio>
 #include <string>
 
-#include "../../include/attn.h"
+#include "attn.h"
 #include "kernels.h"
 
 namespace {

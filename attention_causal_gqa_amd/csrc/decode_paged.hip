@@ -81,10 +81,10 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const bf16* __restric
     int pid_chunk = -1;
     int my_pid = 0;
 
-    uint4 qv[G];
+    u32x4 qv[G];
 #pragma unroll
     for (int h = 0; h < G; ++h)
-        qv[h] = *reinterpret_cast<const uint4*>(q + ((size_t)b * Hq + kvh * G + h) * D + 8 * c);
+        qv[h] = *reinterpret_cast<const u32x4*>(q + ((size_t)b * Hq + kvh * G + h) * D + 8 * c);
 
     float m[G], l[G], o[G][8];
 #pragma unroll
@@ -96,7 +96,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const bf16* __restric
     }
 
     const size_t slice = (size_t)kPage * D;  // elements per (page, kv head)
-    uint4 kr[TPL], vr[TPL];
+    u32x4 kr[TPL], vr[TPL];
     auto load_page = [&](int p) {
         const int j = p - p0;  // wave-uniform
         if ((j >> 6) != pid_chunk) {
@@ -108,15 +108,15 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const bf16* __restric
         const size_t base = ((size_t)pid * Hkv + kvh) * slice + (size_t)r * D + 8 * c;
 #pragma unroll
         for (int i = 0; i < TPL; ++i) {
-            kr[i] = *reinterpret_cast<const uint4*>(kp + base + (size_t)i * TPI * D);
-            vr[i] = *reinterpret_cast<const uint4*>(vp + base + (size_t)i * TPI * D);
+            kr[i] = *reinterpret_cast<const u32x4*>(kp + base + (size_t)i * TPI * D);
+            vr[i] = *reinterpret_cast<const u32x4*>(vp + base + (size_t)i * TPI * D);
         }
     };
 
     int p = p0 + w;
     if (p < p1) load_page(p);
     while (p < p1) {
-        uint4 kc[TPL], vc[TPL];
+        u32x4 kc[TPL], vc[TPL];
 #pragma unroll
         for (int i = 0; i < TPL; ++i) {
             kc[i] = kr[i];
@@ -139,7 +139,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const bf16* __restric
                 acc = chunk_row_sum<D>(acc);
                 x[i][h] = valid[i] ? acc * c1 : -INFINITY;
             }
-            if (!valid[i]) vc[i] = make_uint4(0, 0, 0, 0);  // unused slots may hold NaN
+            if (!valid[i]) vc[i] = u32x4{0u, 0u, 0u, 0u};  // unused slots may hold NaN
         }
         float vf[TPL][8];
 #pragma unroll

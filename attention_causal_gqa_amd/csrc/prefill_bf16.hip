@@ -22,8 +22,10 @@
 //     is 15 in-lane operations plus one v_permlane32_swap.
 //   * The same accumulator registers, rounded to bf16, are exactly the B
 //     operand of O^T += V^T P^T (the contraction index is relabelled to the
-//     key order the accumulator layout gives).  V is written into LDS
-//     transposed (V^T, d-major) so the A operand is two 8-byte LDS reads.
+//     key order the accumulator layout gives).  V stays row-major in LDS; the
+//     A operand (V^T) comes from two transposing ds_read_b64_tr_b16 reads.
+//   * K and V tiles are stored unpadded with an XOR swizzle of 16-byte
+//     chunks, so both operand read patterns are free of bank conflicts.
 //   * out is normalised by the sum of the same bf16-rounded probabilities
 //     that feed the PV product (v_dot2 with ones), so the weights applied to
 //     V sum exactly to the normaliser; the log-sum-exp uses the fp32 sum.
@@ -44,19 +46,45 @@ namespace {
 constexpr int kRows = 128;  // query rows (token, head pairs) per workgroup
 constexpr int kBN = 64;     // keys per tile
 
+// XOR swizzle of 16-byte chunks within an LDS row of CPR chunks: chunk c of
+// row r is stored at position c ^ swz(r).  With CPR = 16, any 16 consecutive
+// rows read at the same chunk (the K operand reads) hit 16 distinct
+// positions, and the 4-row x 32-byte blocks the transposing V reads touch
+// hit 8 distinct positions: both are free of bank conflicts.
+template <int CPR>
+__device__ __forceinline__ int swz(int r) {
+    if constexpr (CPR == 16) {
+        return ((r & 7) << 1) | ((r >> 3) & 1);
+    } else {
+        return ((r & 3) << 1) | ((r >> 2) & 1);
+    }
+}
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+
+// ds_read_b64_tr_b16: within each group of 16 lanes, lane j points at row
+// j/4, columns 4(j%4)..+3 of a 4 x 16 block of 16-bit values; lane i
+// receives column i of the block's 4 rows.
+__device__ __forceinline__ u32x2 lds_read_tr16(const char* p) {
+    v4i16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) v4i16*)(p));
+    return __builtin_bit_cast(u32x2, r);
+}
+
 template <int D, bool kPosScale>
 __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                                                               const bf16* __restrict__ v, bf16* __restrict__ out,
                                                               float* __restrict__ lse, int B, int Hq, int Hkv, int T,
                                                               int G, int BMt, int nqb, float c1) {
-    constexpr int KS = D + 8;      // bf16 per K row in LDS (16-byte pad: conflict-free 16-byte reads)
-    constexpr int VS = kBN + 4;    // bf16 per V^T row in LDS (8-byte pad)
-    constexpr int CPR = D / 8;     // 16-byte chunks per key row
-    constexpr int KPT = D / 32;    // keys per thread in a tile load
-    constexpr int NKK = D / 16;    // k-steps of QK^T
-    constexpr int NMB = D / 32;    // 32-row blocks of O^T
-    __shared__ __attribute__((aligned(16))) bf16 Ks[2][kBN * KS];
-    __shared__ __attribute__((aligned(16))) bf16 Vt[2][D * VS];
+    constexpr int CPR = D / 8;          // 16-byte chunks per key row
+    constexpr int ROWB = D * 2;         // bytes per key row (no padding: rows are swizzled)
+    constexpr int TILEB = kBN * ROWB;   // bytes per K or V tile
+    constexpr int RPL = 256 / CPR;      // rows one pass of the 256 threads covers
+    constexpr int NLD = kBN / RPL;      // 16-byte loads per thread per tile per tensor
+    constexpr int NKK = D / 16;         // k-steps of QK^T
+    constexpr int NMB = D / 32;         // 32-row blocks of O^T
+    __shared__ __attribute__((aligned(16))) char Ks[2][TILEB];
+    __shared__ __attribute__((aligned(16))) char Vs[2][TILEB];
 
     const int tid = threadIdx.x;
     const int w = tid >> 6;
@@ -87,45 +115,59 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(const bf16* __rest
         for (int kk = 0; kk < NKK; ++kk) qreg[kk] = *reinterpret_cast<const bf16x8*>(qrow + 16 * kk);
     }
 
-    // Tile-load role: keys kg*KPT .. +KPT-1, 16-byte chunk c of each.
-    const int kg = tid / CPR;
-    const int c = tid % CPR;
-    const bf16* kbase = k + (size_t)(b * Hkv + kvh) * T * D;
-    const bf16* vbase = v + (size_t)(b * Hkv + kvh) * T * D;
-    uint4 kr[KPT], vr[KPT];
-
-    auto gload = [&](int k0) {
+    // Tile loads: thread -> (row, chunk); a wave stores whole rows, so the
+    // swizzled 16-byte LDS writes of 16 consecutive lanes cover one row.
+    const int ld_c = tid % CPR;
+    const int ld_r0 = tid / CPR;  // rows ld_r0 + RPL*j
+    const bf16* kbase = k + (size_t)(b * Hkv + kvh) * T * D + 8 * ld_c;
+    const bf16* vbase = v + (size_t)(b * Hkv + kvh) * T * D + 8 * ld_c;
+    u32x4 kr[NLD], vr[NLD];
+    // Keys past T are read as key T-1: they are masked for every stored row
+    // (key >= T > token), and V is finite, so they add exact zeros.
+    auto gload = [&](int k0) __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < KPT; ++i) {
-            const int key = k0 + kg * KPT + i;
-            if (key < T) {
-                kr[i] = *reinterpret_cast<const uint4*>(kbase + (size_t)key * D + 8 * c);
-                vr[i] = *reinterpret_cast<const uint4*>(vbase + (size_t)key * D + 8 * c);
-            } else {
-                kr[i] = make_uint4(0, 0, 0, 0);
-                vr[i] = make_uint4(0, 0, 0, 0);
-            }
+        for (int j = 0; j < NLD; ++j) {
+            const int key = min(k0 + ld_r0 + RPL * j, T - 1);
+            kr[j] = *reinterpret_cast<const u32x4*>(kbase + (size_t)key * D);
+            vr[j] = *reinterpret_cast<const u32x4*>(vbase + (size_t)key * D);
         }
     };
-    auto lstore = [&](int buf) {
+    auto lstore = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < KPT; ++i)
-            *reinterpret_cast<uint4*>(&Ks[buf][(kg * KPT + i) * KS + 8 * c]) = kr[i];
-        // V^T[d][key]: element e of chunk c is d = 8c + e; gather it from the KPT keys.
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            uint32_t wv[KPT];
-#pragma unroll
-            for (int i = 0; i < KPT; ++i) {
-                const uint32_t word = (e >> 1) == 0 ? vr[i].x : (e >> 1) == 1 ? vr[i].y : (e >> 1) == 2 ? vr[i].z : vr[i].w;
-                wv[i] = (e & 1) ? (word >> 16) : (word & 0xffffu);
-            }
-            bf16* dst = &Vt[buf][(8 * c + e) * VS + kg * KPT];
-            if constexpr (KPT == 4) {
-                *reinterpret_cast<uint2*>(dst) = make_uint2(wv[0] | (wv[1] << 16), wv[2] | (wv[3] << 16));
-            } else {
-                *reinterpret_cast<uint32_t*>(dst) = wv[0] | (wv[1] << 16);
-            }
+        for (int j = 0; j < NLD; ++j) {
+            const int row = ld_r0 + RPL * j;
+            const int off = row * ROWB + ((ld_c ^ swz<CPR>(row)) << 4);
+            *reinterpret_cast<u32x4*>(&Ks[buf][off]) = kr[j];
+            *reinterpret_cast<u32x4*>(&Vs[buf][off]) = vr[j];
+        }
+    };
+
+    // K operand reads (A of S^T): row 32kb + l32, chunk 2kk + hi.  The row's
+    // swizzle does not depend on kb, so the offset is kread ^ (kk << 5) plus
+    // the row block 32kb * ROWB.
+    const int kread = l32 * ROWB + ((hi ^ swz<CPR>(l32)) << 4);
+    // V operand reads (A of O^T, transposing): lane i = lane % 16 of group
+    // g = lane / 16 reads row 32kb + 16kc + 8h + rl, rl = 4hi + i/4, 8 bytes
+    // at column 32mb + 16(g%2) + 4(i%4).  See vread_off for the swizzle.
+    const int vi = lane & 15;
+    const int vgd = (lane >> 4) & 1;
+    const int vrl = 4 * hi + (vi >> 2);
+    const int vx = 2 * vgd + ((vi & 3) >> 1);  // chunk within the 64-byte column block
+    int vbase_off;
+    if constexpr (CPR == 16) {
+        vbase_off = vrl * ROWB + ((vx ^ (vrl << 1)) << 4) + 8 * (vi & 1);
+    } else {
+        vbase_off = vrl * ROWB + ((vx ^ swz<CPR>(vrl)) << 4) + 8 * (vi & 1);
+    }
+    // Offset of the (mb, kb, kc, h) read: rows R0 = 32kb + 16kc + 8h.
+    auto vread_off = [&](int mb, int kb, int kc, int h) __attribute__((always_inline)) {
+        const int R0 = 32 * kb + 16 * kc + 8 * h;
+        if constexpr (CPR == 16) {
+            // swz(R0 + rl) = (rl << 1) | h; chunk 4mb + vx -> (4mb ^ h) ^ (vx ^ (rl << 1))
+            return R0 * ROWB + (vbase_off ^ (((4 * mb) ^ h) << 4));
+        } else {
+            // swz(R0 + rl) = swz(rl) (R0 is a multiple of 8); chunk 4mb + vx
+            return R0 * ROWB + (vbase_off ^ ((4 * mb) << 4));
         }
     };
 
@@ -152,8 +194,8 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(const bf16* __rest
         const int k0 = t * kBN;
         if (t + 1 < ntiles) gload(k0 + kBN);
 
-        const bf16* Kc = Ks[cur];
-        const bf16* Vc = Vt[cur];
+        const char* Kc = Ks[cur];
+        const char* Vc = Vs[cur];
 
         // S^T tile (64 keys x 32 query columns) as two 32x32 blocks.
         f32x16 sacc[2];
@@ -163,9 +205,10 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(const bf16* __rest
             for (int i = 0; i < 16; ++i) sacc[kb][i] = 0.f;
 #pragma unroll
         for (int kk = 0; kk < NKK; ++kk) {
+            const int off = kread ^ (kk << 5);
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
-                const bf16x8 a = *reinterpret_cast<const bf16x8*>(Kc + (32 * kb + l32) * KS + 16 * kk + 8 * hi);
+                const bf16x8 a = *reinterpret_cast<const bf16x8*>(Kc + kb * 32 * ROWB + off);
                 sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[kk], sacc[kb], 0, 0, 0);
             }
         }
@@ -177,14 +220,15 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(const bf16* __rest
                 for (int i = 0; i < 16; ++i) sacc[kb][i] *= c1;
         }
         // Causal mask on tiles that reach past the workgroup's first token.
-        // Element i of block kb is key k0 + 32kb + 8(i/4) + 4hi + i%4.
+        // Element i of block kb is key k0 + 32kb + 8(i/4) + 4hi + i%4: masked
+        // when 32kb + 8(i/4) + i%4 > token - k0 - 4hi.
         if (k0 + kBN - 1 > t0) {
+            const int thr = token - k0 - 4 * hi;
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
-                    const int key = k0 + 32 * kb + 8 * (i >> 2) + 4 * hi + (i & 3);
-                    if (key > token) sacc[kb][i] = -INFINITY;
+                    if (32 * kb + 8 * (i >> 2) + (i & 3) > thr) sacc[kb][i] = -INFINITY;
                 }
         }
 
@@ -233,18 +277,17 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(const bf16* __rest
 
         // O^T (d x 32 queries) += V^T (d x 64 keys) P^T (64 keys x 32 queries).
         // B element j of (kb, kc) is key 32kb + 16kc + 8(j/4) + 4hi + j%4; the
-        // A operand reads V^T at the same keys.
+        // two transposing reads give V^T at exactly those keys.
 #pragma unroll
         for (int mb = 0; mb < NMB; ++mb) {
-            const bf16* vrow = Vc + (32 * mb + l32) * VS + 4 * hi;
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                 for (int kc = 0; kc < 2; ++kc) {
-                    const uint2 lo = *reinterpret_cast<const uint2*>(vrow + 32 * kb + 16 * kc);
-                    const uint2 hv = *reinterpret_cast<const uint2*>(vrow + 32 * kb + 16 * kc + 8);
-                    const uint4 av = make_uint4(lo.x, lo.y, hv.x, hv.y);
-                    const uint4 bv = make_uint4(pb[kb][kc][0], pb[kb][kc][1], pb[kb][kc][2], pb[kb][kc][3]);
+                    const u32x2 lo = lds_read_tr16(Vc + vread_off(mb, kb, kc, 0));
+                    const u32x2 hv = lds_read_tr16(Vc + vread_off(mb, kb, kc, 1));
+                    const u32x4 av = {lo.x, lo.y, hv.x, hv.y};
+                    const u32x4 bv = {pb[kb][kc][0], pb[kb][kc][1], pb[kb][kc][2], pb[kb][kc][3]};
                     oacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av),
                                                                        __builtin_bit_cast(bf16x8, bv), oacc[mb], 0, 0, 0);
                 }
@@ -254,7 +297,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(const bf16* __rest
         __syncthreads();
     }
 
-    // Epilogue: lanes l and l^32 hold halves of the row sum.
+    // Epilogue: lanes l and l^32 hold halves of the row sums.
     const float lt = pair_sum(l_run);
     const float ll = pair_sum(l_lse);
     if (row_ok) {
@@ -265,9 +308,9 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(const bf16* __rest
         for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
             for (int g4 = 0; g4 < 4; ++g4) {
-                const uint2 wv = make_uint2(pack_bf16x2(oacc[mb][4 * g4] * inv, oacc[mb][4 * g4 + 1] * inv),
-                                            pack_bf16x2(oacc[mb][4 * g4 + 2] * inv, oacc[mb][4 * g4 + 3] * inv));
-                *reinterpret_cast<uint2*>(orow + 32 * mb + 8 * g4) = wv;
+                const u32x2 wv = {pack_bf16x2(oacc[mb][4 * g4] * inv, oacc[mb][4 * g4 + 1] * inv),
+                                  pack_bf16x2(oacc[mb][4 * g4 + 2] * inv, oacc[mb][4 * g4 + 3] * inv)};
+                *reinterpret_cast<u32x2*>(orow + 32 * mb + 8 * g4) = wv;
             }
         if (lse != nullptr && hi == 0) lse[(size_t)(b * Hq + head) * T + token] = (m_run + log2f(ll)) * kLn2;
     }
