@@ -32,8 +32,9 @@
 //   * The running max is only moved when a tile's max exceeds it by more
 //     than 8 (a factor 256 in base 2): rescaling O is then rare, and
 //     probabilities stay below 256, well inside fp32 and bf16 range.
-//   * K/V tiles are double-buffered in LDS: the next tile's global loads are
-//     in flight while the current tile is multiplied.
+//   * K/V tiles go from HBM straight into LDS (global_load_lds_dwordx4, no
+//     staging registers), double-buffered; the loop is software-pipelined so
+//     the QK^T MFMAs of tile t+1 are issued next to the softmax of tile t.
 //   * Workgroups are launched heaviest first (last query blocks have the
 //     most keys); consecutive workgroup ids cycle over (batch, kv head) so a
 //     kv head's blocks fall on the same XCD and share its L2.
@@ -71,6 +72,14 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const char* p) {
     return __builtin_bit_cast(u32x2, r);
 }
 
+// 16 bytes per lane from global memory straight into LDS (global_load_lds
+// dwordx4): lane l's data lands at lds_base + 16 l; lds_base must be the
+// same for the whole wave.
+__device__ __forceinline__ void dma16(const void* g, char* lds_base) {
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
+                                     (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
+}
+
 template <int D, bool kPosScale>
 __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                                                               const bf16* __restrict__ v, bf16* __restrict__ out,
@@ -79,12 +88,16 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(const bf16* __rest
     constexpr int CPR = D / 8;          // 16-byte chunks per key row
     constexpr int ROWB = D * 2;         // bytes per key row (no padding: rows are swizzled)
     constexpr int TILEB = kBN * ROWB;   // bytes per K or V tile
-    constexpr int RPL = 256 / CPR;      // rows one pass of the 256 threads covers
-    constexpr int NLD = kBN / RPL;      // 16-byte loads per thread per tile per tensor
+    constexpr int RPI = 64 / CPR;       // rows one 1 KiB wave-wide DMA covers
+    constexpr int NIW = kBN / (4 * RPI);  // DMAs per wave per tile per tensor
     constexpr int NKK = D / 16;         // k-steps of QK^T
     constexpr int NMB = D / 32;         // 32-row blocks of O^T
-    __shared__ __attribute__((aligned(16))) char Ks[2][TILEB];
-    __shared__ __attribute__((aligned(16))) char Vs[2][TILEB];
+    // Four distinct arrays (not one indexed array) so that the compiler can
+    // tell the asynchronous DMA into one buffer from the reads of another.
+    __shared__ __attribute__((aligned(1024))) char Ks0[TILEB];
+    __shared__ __attribute__((aligned(1024))) char Ks1[TILEB];
+    __shared__ __attribute__((aligned(1024))) char Vs0[TILEB];
+    __shared__ __attribute__((aligned(1024))) char Vs1[TILEB];
 
     const int tid = threadIdx.x;
     const int w = tid >> 6;
@@ -115,30 +128,29 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(const bf16* __rest
         for (int kk = 0; kk < NKK; ++kk) qreg[kk] = *reinterpret_cast<const bf16x8*>(qrow + 16 * kk);
     }
 
-    // Tile loads: thread -> (row, chunk); a wave stores whole rows, so the
-    // swizzled 16-byte LDS writes of 16 consecutive lanes cover one row.
-    const int ld_c = tid % CPR;
-    const int ld_r0 = tid / CPR;  // rows ld_r0 + RPL*j
-    const bf16* kbase = k + (size_t)(b * Hkv + kvh) * T * D + 8 * ld_c;
-    const bf16* vbase = v + (size_t)(b * Hkv + kvh) * T * D + 8 * ld_c;
-    u32x4 kr[NLD], vr[NLD];
+    // Tile DMA: wave-wide DMA n (0 .. 4*NIW-1) fills LDS bytes [1024n, 1024n + 1024),
+    // i.e. rows RPI*n .. RPI*n + RPI-1; lane l lands at row RPI*n + l / CPR,
+    // swizzled position l % CPR, so it fetches logical chunk (l % CPR) ^ swz(row).
+    const bf16* kbase = k + (size_t)(b * Hkv + kvh) * T * D;
+    const bf16* vbase = v + (size_t)(b * Hkv + kvh) * T * D;
+    int drow[NIW], dcol[NIW];
+#pragma unroll
+    for (int j = 0; j < NIW; ++j) {
+        drow[j] = RPI * (w * NIW + j) + lane / CPR;
+        dcol[j] = 8 * ((lane % CPR) ^ swz<CPR>(drow[j]));
+    }
     // Keys past T are read as key T-1: they are masked for every stored row
     // (key >= T > token), and V is finite, so they add exact zeros.
-    auto gload = [&](int k0) __attribute__((always_inline)) {
+    auto dma_tile = [&](const bf16* base, char* dst, int k0) __attribute__((always_inline)) {
+        if (k0 + kBN <= T) {
+            const bf16* tb = base + (size_t)k0 * D;
 #pragma unroll
-        for (int j = 0; j < NLD; ++j) {
-            const int key = min(k0 + ld_r0 + RPL * j, T - 1);
-            kr[j] = *reinterpret_cast<const u32x4*>(kbase + (size_t)key * D);
-            vr[j] = *reinterpret_cast<const u32x4*>(vbase + (size_t)key * D);
-        }
-    };
-    auto lstore = [&](int buf) __attribute__((always_inline)) {
+            for (int j = 0; j < NIW; ++j)
+                dma16(tb + drow[j] * D + dcol[j], dst + 1024 * (w * NIW + j));
+        } else {
 #pragma unroll
-        for (int j = 0; j < NLD; ++j) {
-            const int row = ld_r0 + RPL * j;
-            const int off = row * ROWB + ((ld_c ^ swz<CPR>(row)) << 4);
-            *reinterpret_cast<u32x4*>(&Ks[buf][off]) = kr[j];
-            *reinterpret_cast<u32x4*>(&Vs[buf][off]) = vr[j];
+            for (int j = 0; j < NIW; ++j)
+                dma16(base + (size_t)min(k0 + drow[j], T - 1) * D + dcol[j], dst + 1024 * (w * NIW + j));
         }
     };
 
@@ -148,7 +160,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(const bf16* __rest
     const int kread = l32 * ROWB + ((hi ^ swz<CPR>(l32)) << 4);
     // V operand reads (A of O^T, transposing): lane i = lane % 16 of group
     // g = lane / 16 reads row 32kb + 16kc + 8h + rl, rl = 4hi + i/4, 8 bytes
-    // at column 32mb + 16(g%2) + 4(i%4).  See vread_off for the swizzle.
+    // at column 32mb + 16(g%2) + 4(i%4).
     const int vi = lane & 15;
     const int vgd = (lane >> 4) & 1;
     const int vrl = 4 * hi + (vi >> 2);
@@ -159,7 +171,6 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(const bf16* __rest
     } else {
         vbase_off = vrl * ROWB + ((vx ^ swz<CPR>(vrl)) << 4) + 8 * (vi & 1);
     }
-    // Offset of the (mb, kb, kc, h) read: rows R0 = 32kb + 16kc + 8h.
     auto vread_off = [&](int mb, int kb, int kc, int h) __attribute__((always_inline)) {
         const int R0 = 32 * kb + 16 * kc + 8 * h;
         if constexpr (CPR == 16) {
@@ -168,6 +179,22 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(const bf16* __rest
         } else {
             // swz(R0 + rl) = swz(rl) (R0 is a multiple of 8); chunk 4mb + vx
             return R0 * ROWB + (vbase_off ^ ((4 * mb) << 4));
+        }
+    };
+
+    auto qk = [&](const char* Kc, f32x16 (&sacc)[2]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) sacc[kb][i] = 0.f;
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) {
+            const int off = kread ^ (kk << 5);
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                const bf16x8 a = *reinterpret_cast<const bf16x8*>(Kc + kb * 32 * ROWB + off);
+                sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[kk], sacc[kb], 0, 0, 0);
+            }
         }
     };
 
@@ -185,34 +212,9 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(const bf16* __rest
     const int ntiles = (kend + kBN - 1) / kBN;
     constexpr uint32_t kOnes = 0x3F803F80u;  // two bf16 1.0
 
-    gload(0);
-    lstore(0);
-    __syncthreads();
-
-    for (int t = 0; t < ntiles; ++t) {
-        const int cur = t & 1;
+    // softmax of tile t (scores in sacc) and O += P V from Vc.
+    auto softmax_pv = [&](int t, f32x16 (&sacc)[2], const char* Vc) __attribute__((always_inline)) {
         const int k0 = t * kBN;
-        if (t + 1 < ntiles) gload(k0 + kBN);
-
-        const char* Kc = Ks[cur];
-        const char* Vc = Vs[cur];
-
-        // S^T tile (64 keys x 32 query columns) as two 32x32 blocks.
-        f32x16 sacc[2];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) sacc[kb][i] = 0.f;
-#pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) {
-            const int off = kread ^ (kk << 5);
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                const bf16x8 a = *reinterpret_cast<const bf16x8*>(Kc + kb * 32 * ROWB + off);
-                sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[kk], sacc[kb], 0, 0, 0);
-            }
-        }
-
         if constexpr (!kPosScale) {
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
@@ -231,7 +233,6 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(const bf16* __rest
                     if (32 * kb + 8 * (i >> 2) + (i & 3) > thr) sacc[kb][i] = -INFINITY;
                 }
         }
-
         float mx = -INFINITY;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
@@ -256,7 +257,6 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(const bf16* __rest
                 for (int i = 0; i < 16; ++i) oacc[mb][i] *= alpha;
             m_run = mn;
         }
-
         // P^T in bf16: B operand of the PV product.  Two row sums: over the
         // rounded values (so the weights applied to V sum exactly to the
         // normaliser of out) and over the fp32 values (the log-sum-exp, which
@@ -274,7 +274,6 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(const bf16* __rest
                     l_run = dot2_bf16(pb[kb][kc][jj], kOnes, l_run);
                     l_lse += p0 + p1;
                 }
-
         // O^T (d x 32 queries) += V^T (d x 64 keys) P^T (64 keys x 32 queries).
         // B element j of (kb, kc) is key 32kb + 16kc + 8(j/4) + 4hi + j%4; the
         // two transposing reads give V^T at exactly those keys.
@@ -292,9 +291,35 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(const bf16* __rest
                                                                        __builtin_bit_cast(bf16x8, bv), oacc[mb], 0, 0, 0);
                 }
         }
+    };
 
-        if (t + 1 < ntiles) lstore(cur ^ 1);
+    // Software pipeline: iteration t multiplies K(t+1) (scores for the next
+    // tile) while it runs the softmax of tile t and multiplies V(t); the DMA
+    // of V(t+1) and K(t+2) is in flight meanwhile.  Buffers: K(t) in Ks[t%2],
+    // V(t) in Vs[t%2].
+    f32x16 s_cur[2], s_nxt[2];
+    dma_tile(kbase, Ks0, 0);
+    dma_tile(vbase, Vs0, 0);
+    if (ntiles > 1) dma_tile(kbase, Ks1, kBN);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    qk(Ks0, s_cur);
+    __syncthreads();  // every wave is done with Ks0 before K(2) is written into it
+
+    auto step = [&](int t, const char* Kn, char* Kdst, const char* Vc, char* Vdst) __attribute__((always_inline)) {
+        if (t + 1 < ntiles) dma_tile(vbase, Vdst, (t + 1) * kBN);
+        if (t + 2 < ntiles) dma_tile(kbase, Kdst, (t + 2) * kBN);
+        if (t + 1 < ntiles) qk(Kn, s_nxt);
+        softmax_pv(t, s_cur, Vc);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) s_cur[kb] = s_nxt[kb];
+        __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
+    };
+    for (int t = 0; t < ntiles; t += 2) {
+        step(t, Ks1, Ks0, Vs0, Vs1);
+        if (t + 1 >= ntiles) break;
+        step(t + 1, Ks0, Ks1, Vs1, Vs0);
     }
 
     // Epilogue: lanes l and l^32 hold halves of the row sums.
