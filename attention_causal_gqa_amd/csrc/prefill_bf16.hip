@@ -33,8 +33,11 @@
 //     than 8 (a factor 256 in base 2): rescaling O is then rare, and
 //     probabilities stay below 256, well inside fp32 and bf16 range.
 //   * K/V tiles go from HBM straight into LDS (global_load_lds_dwordx4, no
-//     staging registers), double-buffered; the loop is software-pipelined so
-//     the QK^T MFMAs of tile t+1 are issued next to the softmax of tile t.
+//     staging registers), double-buffered: the next tile's DMA is in flight
+//     while the current tile is multiplied.  Two waves share each SIMD, so
+//     one wave's softmax overlaps the other's MFMAs.
+//   * The causal mask runs, behind a wave-uniform branch, only on the tiles
+//     that reach past the workgroup's first token.
 //   * Workgroups are launched heaviest first (last query blocks have the
 //     most keys); consecutive workgroup ids cycle over (batch, kv head) so a
 //     kv head's blocks fall on the same XCD and share its L2.
@@ -48,14 +51,16 @@ constexpr int kRows = 128;  // query rows (token, head pairs) per workgroup
 constexpr int kBN = 64;     // keys per tile
 
 // XOR swizzle of 16-byte chunks within an LDS row of CPR chunks: chunk c of
-// row r is stored at position c ^ swz(r).  With CPR = 16, any 16 consecutive
-// rows read at the same chunk (the K operand reads) hit 16 distinct
-// positions, and the 4-row x 32-byte blocks the transposing V reads touch
-// hit 8 distinct positions: both are free of bank conflicts.
+// row r is stored at position c ^ swz(r).  With CPR = 16 (256-byte rows),
+// swz(r) = 4(r%4) + (r/4)%4: 16 consecutive rows read at one chunk (the K
+// operand reads, 16 lanes x 16 bytes) hit 16 distinct positions, and 4
+// consecutive rows read over 64 aligned bytes (the transposing V reads,
+// 32 lanes x 8 bytes) land in 4 distinct 64-byte blocks, so neither pattern
+// has LDS bank conflicts.
 template <int CPR>
 __device__ __forceinline__ int swz(int r) {
     if constexpr (CPR == 16) {
-        return ((r & 7) << 1) | ((r >> 3) & 1);
+        return ((r & 3) << 2) | ((r >> 2) & 3);
     } else {
         return ((r & 3) << 1) | ((r >> 2) & 1);
     }
@@ -93,14 +98,15 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(const bf16* __rest
     constexpr int NKK = D / 16;         // k-steps of QK^T
     constexpr int NMB = D / 32;         // 32-row blocks of O^T
     // Four distinct arrays (not one indexed array) so that the compiler can
-    // tell the asynchronous DMA into one buffer from the reads of another.
+    // tell the asynchronous DMA into one buffer from the reads of another and
+    // does not make LDS reads wait for it.
     __shared__ __attribute__((aligned(1024))) char Ks0[TILEB];
     __shared__ __attribute__((aligned(1024))) char Ks1[TILEB];
     __shared__ __attribute__((aligned(1024))) char Vs0[TILEB];
     __shared__ __attribute__((aligned(1024))) char Vs1[TILEB];
 
     const int tid = threadIdx.x;
-    const int w = tid >> 6;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, in an SGPR
     const int lane = tid & 63;
     const int l32 = lane & 31;
     const int hi = lane >> 5;
@@ -133,24 +139,27 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(const bf16* __rest
     // swizzled position l % CPR, so it fetches logical chunk (l % CPR) ^ swz(row).
     const bf16* kbase = k + (size_t)(b * Hkv + kvh) * T * D;
     const bf16* vbase = v + (size_t)(b * Hkv + kvh) * T * D;
-    int drow[NIW], dcol[NIW];
+    int drow[NIW];
+    uint32_t doff[NIW];  // byte offset of the lane's chunk within a tile of rows
 #pragma unroll
     for (int j = 0; j < NIW; ++j) {
         drow[j] = RPI * (w * NIW + j) + lane / CPR;
-        dcol[j] = 8 * ((lane % CPR) ^ swz<CPR>(drow[j]));
+        doff[j] = (uint32_t)(drow[j] * ROWB + 16 * ((lane % CPR) ^ swz<CPR>(drow[j])));
     }
     // Keys past T are read as key T-1: they are masked for every stored row
     // (key >= T > token), and V is finite, so they add exact zeros.
     auto dma_tile = [&](const bf16* base, char* dst, int k0) __attribute__((always_inline)) {
         if (k0 + kBN <= T) {
-            const bf16* tb = base + (size_t)k0 * D;
+            const char* tb = reinterpret_cast<const char*>(base + (size_t)k0 * D);
 #pragma unroll
-            for (int j = 0; j < NIW; ++j)
-                dma16(tb + drow[j] * D + dcol[j], dst + 1024 * (w * NIW + j));
+            for (int j = 0; j < NIW; ++j) dma16(tb + doff[j], dst + 1024 * (w * NIW + j));
         } else {
+            const char* bb = reinterpret_cast<const char*>(base);
 #pragma unroll
-            for (int j = 0; j < NIW; ++j)
-                dma16(base + (size_t)min(k0 + drow[j], T - 1) * D + dcol[j], dst + 1024 * (w * NIW + j));
+            for (int j = 0; j < NIW; ++j) {
+                const int key = min(k0 + drow[j], T - 1);
+                dma16(bb + (size_t)key * ROWB + (doff[j] - (uint32_t)(drow[j] * ROWB)), dst + 1024 * (w * NIW + j));
+            }
         }
     };
 
@@ -167,15 +176,16 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(const bf16* __rest
     const int vx = 2 * vgd + ((vi & 3) >> 1);  // chunk within the 64-byte column block
     int vbase_off;
     if constexpr (CPR == 16) {
-        vbase_off = vrl * ROWB + ((vx ^ (vrl << 1)) << 4) + 8 * (vi & 1);
+        // Row R0 + vrl (R0 = 32kb + 16kc + 8h) has swz = 4(vi/4) + 2h + hi, so
+        // chunk 4mb + vx sits at 4(mb ^ vi/4) + (vx ^ hi ^ 2h).
+        vbase_off = vrl * ROWB + 64 * (vi >> 2) + 16 * (vx ^ hi) + 8 * (vi & 1);
     } else {
         vbase_off = vrl * ROWB + ((vx ^ swz<CPR>(vrl)) << 4) + 8 * (vi & 1);
     }
     auto vread_off = [&](int mb, int kb, int kc, int h) __attribute__((always_inline)) {
         const int R0 = 32 * kb + 16 * kc + 8 * h;
         if constexpr (CPR == 16) {
-            // swz(R0 + rl) = (rl << 1) | h; chunk 4mb + vx -> (4mb ^ h) ^ (vx ^ (rl << 1))
-            return R0 * ROWB + (vbase_off ^ (((4 * mb) ^ h) << 4));
+            return R0 * ROWB + (vbase_off ^ (64 * mb + 32 * h));
         } else {
             // swz(R0 + rl) = swz(rl) (R0 is a multiple of 8); chunk 4mb + vx
             return R0 * ROWB + (vbase_off ^ ((4 * mb) << 4));
@@ -213,6 +223,8 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(const bf16* __rest
     constexpr uint32_t kOnes = 0x3F803F80u;  // two bf16 1.0
 
     // softmax of tile t (scores in sacc) and O += P V from Vc.
+    // Tiles from first_diag on reach past the workgroup's first token t0.
+    const int first_diag = (t0 + 1) / kBN;
     auto softmax_pv = [&](int t, f32x16 (&sacc)[2], const char* Vc) __attribute__((always_inline)) {
         const int k0 = t * kBN;
         if constexpr (!kPosScale) {
@@ -224,7 +236,10 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(const bf16* __rest
         // Causal mask on tiles that reach past the workgroup's first token.
         // Element i of block kb is key k0 + 32kb + 8(i/4) + 4hi + i%4: masked
         // when 32kb + 8(i/4) + i%4 > token - k0 - 4hi.
-        if (k0 + kBN - 1 > t0) {
+        if (t >= first_diag) {
+            // A real (wave-uniform) branch: the empty volatile asm keeps the
+            // compiler from turning the mask into selects run on every tile.
+            __asm__ volatile("" ::: "memory");
             const int thr = token - k0 - 4 * hi;
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
@@ -297,29 +312,29 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(const bf16* __rest
     // tile) while it runs the softmax of tile t and multiplies V(t); the DMA
     // of V(t+1) and K(t+2) is in flight meanwhile.  Buffers: K(t) in Ks[t%2],
     // V(t) in Vs[t%2].
-    f32x16 s_cur[2], s_nxt[2];
+    // Double-buffered tiles: iteration t reads K(t), V(t) from buffer t%2
+    // while the DMA of tile t+1 into the other buffer is in flight.  Two
+    // waves share each SIMD, so one wave's softmax overlaps the other's MFMAs.
     dma_tile(kbase, Ks0, 0);
     dma_tile(vbase, Vs0, 0);
-    if (ntiles > 1) dma_tile(kbase, Ks1, kBN);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    qk(Ks0, s_cur);
-    __syncthreads();  // every wave is done with Ks0 before K(2) is written into it
 
-    auto step = [&](int t, const char* Kn, char* Kdst, const char* Vc, char* Vdst) __attribute__((always_inline)) {
-        if (t + 1 < ntiles) dma_tile(vbase, Vdst, (t + 1) * kBN);
-        if (t + 2 < ntiles) dma_tile(kbase, Kdst, (t + 2) * kBN);
-        if (t + 1 < ntiles) qk(Kn, s_nxt);
-        softmax_pv(t, s_cur, Vc);
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) s_cur[kb] = s_nxt[kb];
+    auto step = [&](int t, const char* Kc, const char* Vc, char* Kdst, char* Vdst) __attribute__((always_inline)) {
+        if (t + 1 < ntiles) {
+            dma_tile(kbase, Kdst, (t + 1) * kBN);
+            dma_tile(vbase, Vdst, (t + 1) * kBN);
+        }
+        f32x16 sacc[2];
+        qk(Kc, sacc);
+        softmax_pv(t, sacc, Vc);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
     };
     for (int t = 0; t < ntiles; t += 2) {
-        step(t, Ks1, Ks0, Vs0, Vs1);
+        step(t, Ks0, Vs0, Ks1, Vs1);
         if (t + 1 >= ntiles) break;
-        step(t + 1, Ks0, Ks1, Vs1, Vs0);
+        step(t + 1, Ks1, Vs1, Ks0, Vs0);
     }
 
     // Epilogue: lanes l and l^32 hold halves of the row sums.
