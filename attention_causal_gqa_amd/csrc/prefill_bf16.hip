@@ -47,7 +47,7 @@
 namespace attn {
 namespace {
 
-constexpr int kRows = 128;  // query rows (token, head pairs) per workgroup
+constexpr int kRows = 256;  // query rows (token, head pairs) per workgroup
 constexpr int kBN = 64;     // keys per tile
 
 // XOR swizzle of 16-byte chunks within an LDS row of CPR chunks: chunk c of
@@ -85,18 +85,33 @@ __device__ __forceinline__ void dma16(const void* g, char* lds_base) {
                                      (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
 }
 
+// Ping-pong schedule.  A workgroup is 8 waves = two groups of 4 (one wave
+// of each group per SIMD), 256 query rows, sharing every K/V tile.  Each
+// iteration t has an MFMA phase (O += P(t-1) V(t-1), then S(t) = K(t) Q^T)
+// and a VALU phase (softmax of S(t) into P(t)), each ended by a workgroup
+// barrier.  Group B passes one extra barrier first, so it runs one phase
+// behind group A: on every SIMD one wave is in its MFMA phase while the
+// other is in its VALU phase, and the barriers keep them that way.
+//
+// Barrier slots (slot s ends with the s-th barrier): group A runs phase 1 of
+// iteration t in slot 2t and phase 2 in slot 2t+1; group B one slot later.
+// K(t) and V(t-1) are read in slots 2t (A) and 2t+1 (B).  The DMA of K(t+1)
+// and V(t) is issued in slot 2t (group A at the start of its phase 1 of t,
+// group B at the start of its phase 2 of t-1, each for its own rows), into
+// the buffers last read in slots 2t-2 and 2t-1, and each wave waits for its
+// own DMA before the barrier that ends slot 2t+1.
 template <int D, bool kPosScale>
-__global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
+__global__ __launch_bounds__(512, 1) void prefill_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                                                               const bf16* __restrict__ v, bf16* __restrict__ out,
                                                               float* __restrict__ lse, int B, int Hq, int Hkv, int T,
                                                               int G, int BMt, int nqb, float c1) {
-    constexpr int CPR = D / 8;          // 16-byte chunks per key row
-    constexpr int ROWB = D * 2;         // bytes per key row (no padding: rows are swizzled)
-    constexpr int TILEB = kBN * ROWB;   // bytes per K or V tile
-    constexpr int RPI = 64 / CPR;       // rows one 1 KiB wave-wide DMA covers
-    constexpr int NIW = kBN / (4 * RPI);  // DMAs per wave per tile per tensor
-    constexpr int NKK = D / 16;         // k-steps of QK^T
-    constexpr int NMB = D / 32;         // 32-row blocks of O^T
+    constexpr int CPR = D / 8;            // 16-byte chunks per key row
+    constexpr int ROWB = D * 2;           // bytes per key row (no padding: rows are swizzled)
+    constexpr int TILEB = kBN * ROWB;     // bytes per K or V tile
+    constexpr int RPI = 64 / CPR;         // rows one 1 KiB wave-wide DMA covers
+    constexpr int NIW = kBN / (8 * RPI);  // DMAs per wave per tile per tensor
+    constexpr int NKK = D / 16;           // k-steps of QK^T
+    constexpr int NMB = D / 32;           // 32-row blocks of O^T
     // Four distinct arrays (not one indexed array) so that the compiler can
     // tell the asynchronous DMA into one buffer from the reads of another and
     // does not make LDS reads wait for it.
@@ -106,7 +121,8 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(const bf16* __rest
     __shared__ __attribute__((aligned(1024))) char Vs1[TILEB];
 
     const int tid = threadIdx.x;
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, in an SGPR
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index 0..7, in an SGPR
+    const int grp = w >> 2;                                  // 0: group A, 1: group B
     const int lane = tid & 63;
     const int l32 = lane & 31;
     const int hi = lane >> 5;
@@ -118,7 +134,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(const bf16* __rest
     const int kvh = pair % Hkv;
     const int t0 = qb * BMt;
 
-    // This lane's query column: row r of the workgroup.
+    // This lane's query column: row r of the workgroup (256 rows).
     const int r = 32 * w + l32;
     const int tt = r / G;
     const int head = kvh * G + (r % G);
@@ -134,9 +150,10 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(const bf16* __rest
         for (int kk = 0; kk < NKK; ++kk) qreg[kk] = *reinterpret_cast<const bf16x8*>(qrow + 16 * kk);
     }
 
-    // Tile DMA: wave-wide DMA n (0 .. 4*NIW-1) fills LDS bytes [1024n, 1024n + 1024),
+    // Tile DMA: wave-wide DMA n (0 .. 8*NIW-1) fills LDS bytes [1024n, 1024n + 1024),
     // i.e. rows RPI*n .. RPI*n + RPI-1; lane l lands at row RPI*n + l / CPR,
     // swizzled position l % CPR, so it fetches logical chunk (l % CPR) ^ swz(row).
+    // Wave w owns DMAs w*NIW .. w*NIW + NIW-1 of every tile.
     const bf16* kbase = k + (size_t)(b * Hkv + kvh) * T * D;
     const bf16* vbase = v + (size_t)(b * Hkv + kvh) * T * D;
     int drow[NIW];
@@ -192,27 +209,13 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(const bf16* __rest
         }
     };
 
-    auto qk = [&](const char* Kc, f32x16 (&sacc)[2]) __attribute__((always_inline)) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) sacc[kb][i] = 0.f;
-#pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) {
-            const int off = kread ^ (kk << 5);
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                const bf16x8 a = *reinterpret_cast<const bf16x8*>(Kc + kb * 32 * ROWB + off);
-                sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[kk], sacc[kb], 0, 0, 0);
-            }
-        }
-    };
-
     f32x16 oacc[NMB];
 #pragma unroll
     for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) oacc[mb][i] = 0.f;
+    f32x16 sacc[2];           // S^T of the current tile (64 keys x 32 query columns)
+    uint32_t pb[2][2][4];     // P^T of the previous tile in bf16 (B operand of PV)
     float m_run = -INFINITY;  // running max, base-2 scaled domain
     float l_run = 0.f;        // this lane's share of the row sum of bf16-rounded p (normalises out)
     float l_lse = 0.f;        // the same sum over fp32 p (for the log-sum-exp)
@@ -220,12 +223,68 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(const bf16* __rest
     const float cc = kPosScale ? c1 : 1.f;
     const int kend = min(t0 + BMt, T);
     const int ntiles = (kend + kBN - 1) / kBN;
+    const int first_diag = (t0 + 1) / kBN;   // tiles from here on reach past token t0
     constexpr uint32_t kOnes = 0x3F803F80u;  // two bf16 1.0
 
-    // softmax of tile t (scores in sacc) and O += P V from Vc.
-    // Tiles from first_diag on reach past the workgroup's first token t0.
-    const int first_diag = (t0 + 1) / kBN;
-    auto softmax_pv = [&](int t, f32x16 (&sacc)[2], const char* Vc) __attribute__((always_inline)) {
+    // MFMA phase: O^T += V^T(t-1) P^T(t-1), then S^T(t) = K(t) Q^T.
+    auto mfma_phase = [&](bool do_pv, const char* Vp, bool do_qk, const char* Kc) __attribute__((always_inline)) {
+        if (do_pv) {
+            // B element j of (kb, kc) is key 32kb + 16kc + 8(j/4) + 4hi + j%4;
+            // the two transposing reads give V^T at exactly those keys.
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int kc = 0; kc < 2; ++kc) {
+                    const u32x4 bv = {pb[kb][kc][0], pb[kb][kc][1], pb[kb][kc][2], pb[kb][kc][3]};
+#pragma unroll
+                    for (int mb = 0; mb < NMB; ++mb) {
+                        const u32x2 lo = lds_read_tr16(Vp + vread_off(mb, kb, kc, 0));
+                        const u32x2 hv = lds_read_tr16(Vp + vread_off(mb, kb, kc, 1));
+                        const u32x4 av = {lo.x, lo.y, hv.x, hv.y};
+                        oacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                            __builtin_bit_cast(bf16x8, av), __builtin_bit_cast(bf16x8, bv), oacc[mb], 0, 0, 0);
+                    }
+                }
+            // Schedule: 8 LDS reads ahead, then one MFMA per two new reads, so
+            // the LDS latency hides behind the MFMAs of this same wave.
+            constexpr int NPV = 4 * NMB;  // MFMAs (2 reads each)
+            __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+            for (int i = 0; i < NPV - 4; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+        }
+        if (do_qk) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) sacc[kb][i] = 0.f;
+#pragma unroll
+            for (int kk = 0; kk < NKK; ++kk) {
+                const int off = kread ^ (kk << 5);
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb) {
+                    const bf16x8 a = *reinterpret_cast<const bf16x8*>(Kc + kb * 32 * ROWB + off);
+                    sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[kk], sacc[kb], 0, 0, 0);
+                }
+            }
+            // Schedule: 4 K reads ahead, then one MFMA per new read.
+            constexpr int NQK = 2 * NKK;
+            __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
+#pragma unroll
+            for (int i = 0; i < NQK - 4; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 1);
+        }
+    };
+
+    // VALU phase: softmax of tile t (scores in sacc) into pb, row sums, and
+    // (rarely) the rescale of O.
+    auto softmax_phase = [&](int t) __attribute__((always_inline)) {
         const int k0 = t * kBN;
         if constexpr (!kPosScale) {
 #pragma unroll
@@ -244,22 +303,39 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(const bf16* __rest
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
+                for (int i = 0; i < 16; ++i)
                     if (32 * kb + 8 * (i >> 2) + (i & 3) > thr) sacc[kb][i] = -INFINITY;
-                }
         }
-        float mx = -INFINITY;
+        // Probabilities against the current running max, started before the
+        // row max is known (they only depend on m_run); the max decides below
+        // whether they must be recomputed, which happens only when a tile's
+        // max exceeds m_run by more than 8 (base 2).  In tile 0 m_run = -inf,
+        // so every lane takes that path.
+        float pf[2][16];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
+            for (int i = 0; i < 16; ++i) pf[kb][i] = fast_exp2(fmaf(sacc[kb][i], cc, -m_run));
+        // Row max: a tree of 3-input maxima, then lane l ^ 32.
+        float m3[11];
+#pragma unroll
+        for (int i = 0; i < 10; ++i) {
+            const int a = 3 * i, b2 = 3 * i + 1, c2 = 3 * i + 2;
+            m3[i] = fmaxf(fmaxf(sacc[a >> 4][a & 15], sacc[b2 >> 4][b2 & 15]), sacc[c2 >> 4][c2 & 15]);
+        }
+        m3[10] = fmaxf(sacc[1][14], sacc[1][15]);
+        const float m4a = fmaxf(fmaxf(m3[0], m3[1]), m3[2]);
+        const float m4b = fmaxf(fmaxf(m3[3], m3[4]), m3[5]);
+        const float m4c = fmaxf(fmaxf(m3[6], m3[7]), m3[8]);
+        const float m4d = fmaxf(m3[9], m3[10]);
+        float mx = fmaxf(fmaxf(m4a, m4b), fmaxf(m4c, m4d));
         mx = pair_max(mx);
         const float mt = mx * cc;  // tile max in the base-2 domain
         // Key 0 lies in tile 0 and is visible to every row, so after tile 0
-        // m_run is finite; in tile 0 every lane needs the update.  The branch
-        // is taken by the whole wave, but a lane that does not need it keeps
-        // its max (alpha = 1, exact), so a row's result never depends on the
-        // other rows of its wave.
+        // m_run is finite.  The branch is taken by the whole wave, but a lane
+        // that does not need it keeps its max (alpha = 1, exact) and its
+        // probabilities, so a row's result never depends on the other rows of
+        // its wave.  O holds tiles < t here (PV of t-1 is done).
         const bool grow = mt > m_run + 8.f;
         if (__any(grow)) {
             const float mn = grow ? mt : m_run;
@@ -271,71 +347,71 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(const bf16* __rest
 #pragma unroll
                 for (int i = 0; i < 16; ++i) oacc[mb][i] *= alpha;
             m_run = mn;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) pf[kb][i] = fast_exp2(fmaf(sacc[kb][i], cc, -m_run));
         }
         // P^T in bf16: B operand of the PV product.  Two row sums: over the
         // rounded values (so the weights applied to V sum exactly to the
         // normaliser of out) and over the fp32 values (the log-sum-exp, which
         // bf16 rounding of p would otherwise shift by up to 2^-9 relative).
-        uint32_t pb[2][2][4];
+        float lr[4] = {0.f, 0.f, 0.f, 0.f}, lsum[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int kc = 0; kc < 2; ++kc)
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj) {
-                    const float p0 = fast_exp2(fmaf(sacc[kb][8 * kc + 2 * jj], cc, -m_run));
-                    const float p1 = fast_exp2(fmaf(sacc[kb][8 * kc + 2 * jj + 1], cc, -m_run));
+                    const float p0 = pf[kb][8 * kc + 2 * jj];
+                    const float p1 = pf[kb][8 * kc + 2 * jj + 1];
                     pb[kb][kc][jj] = pack_bf16x2(p0, p1);
-                    l_run = dot2_bf16(pb[kb][kc][jj], kOnes, l_run);
-                    l_lse += p0 + p1;
+                    lr[jj] = dot2_bf16(pb[kb][kc][jj], kOnes, lr[jj]);
+                    lsum[jj] += p0 + p1;
                 }
-        // O^T (d x 32 queries) += V^T (d x 64 keys) P^T (64 keys x 32 queries).
-        // B element j of (kb, kc) is key 32kb + 16kc + 8(j/4) + 4hi + j%4; the
-        // two transposing reads give V^T at exactly those keys.
-#pragma unroll
-        for (int mb = 0; mb < NMB; ++mb) {
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int kc = 0; kc < 2; ++kc) {
-                    const u32x2 lo = lds_read_tr16(Vc + vread_off(mb, kb, kc, 0));
-                    const u32x2 hv = lds_read_tr16(Vc + vread_off(mb, kb, kc, 1));
-                    const u32x4 av = {lo.x, lo.y, hv.x, hv.y};
-                    const u32x4 bv = {pb[kb][kc][0], pb[kb][kc][1], pb[kb][kc][2], pb[kb][kc][3]};
-                    oacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av),
-                                                                       __builtin_bit_cast(bf16x8, bv), oacc[mb], 0, 0, 0);
-                }
-        }
+        l_run += (lr[0] + lr[1]) + (lr[2] + lr[3]);
+        l_lse += (lsum[0] + lsum[1]) + (lsum[2] + lsum[3]);
     };
 
-    // Software pipeline: iteration t multiplies K(t+1) (scores for the next
-    // tile) while it runs the softmax of tile t and multiplies V(t); the DMA
-    // of V(t+1) and K(t+2) is in flight meanwhile.  Buffers: K(t) in Ks[t%2],
-    // V(t) in Vs[t%2].
-    // Double-buffered tiles: iteration t reads K(t), V(t) from buffer t%2
-    // while the DMA of tile t+1 into the other buffer is in flight.  Two
-    // waves share each SIMD, so one wave's softmax overlaps the other's MFMAs.
+    // Prologue: K(0) from all waves; then group B issues its half of
+    // (K(1), V(0)) and takes its offset barrier.
     dma_tile(kbase, Ks0, 0);
-    dma_tile(vbase, Vs0, 0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+    if (grp == 1) {
+        if (1 < ntiles) dma_tile(kbase, Ks1, kBN);
+        dma_tile(vbase, Vs0, 0);
+        __syncthreads();
+    }
 
-    auto step = [&](int t, const char* Kc, const char* Vc, char* Kdst, char* Vdst) __attribute__((always_inline)) {
-        if (t + 1 < ntiles) {
-            dma_tile(kbase, Kdst, (t + 1) * kBN);
-            dma_tile(vbase, Vdst, (t + 1) * kBN);
+    // Iteration t (t = 0 .. ntiles): phase 1 = PV(t-1) + QK(t), phase 2 =
+    // softmax(t).  Buffers: K(t) in Ks[t%2], V(t) in Vs[t%2].
+    auto iteration = [&](int t, const char* Kc, char* Knext, const char* Vprev, char* Vcur, char* Kafter,
+                         char* Vnext) __attribute__((always_inline)) {
+        // ---- phase 1
+        if (grp == 0) {
+            if (t + 1 < ntiles) dma_tile(kbase, Knext, (t + 1) * kBN);
+            if (t < ntiles) dma_tile(vbase, Vcur, t * kBN);
         }
-        f32x16 sacc[2];
-        qk(Kc, sacc);
-        softmax_pv(t, sacc, Vc);
-        __builtin_amdgcn_s_waitcnt(0);
+        mfma_phase(t > 0, Vprev, t < ntiles, Kc);
+        if (grp == 1) __builtin_amdgcn_s_waitcnt(0);  // group B's DMA of (K(t+1), V(t))
+        __syncthreads();
+        // ---- phase 2
+        if (grp == 1) {
+            if (t + 2 < ntiles) dma_tile(kbase, Kafter, (t + 2) * kBN);
+            if (t + 1 < ntiles) dma_tile(vbase, Vnext, (t + 1) * kBN);
+        }
+        if (t < ntiles) softmax_phase(t);
+        if (grp == 0) __builtin_amdgcn_s_waitcnt(0);  // group A's DMA of (K(t+1), V(t))
         __syncthreads();
     };
-    for (int t = 0; t < ntiles; t += 2) {
-        step(t, Ks0, Vs0, Ks1, Vs1);
-        if (t + 1 >= ntiles) break;
-        step(t + 1, Ks1, Vs1, Ks0, Vs0);
+    for (int t = 0; t <= ntiles; t += 2) {
+        // t even: K(t) in Ks0, K(t+1) -> Ks1, V(t-1) in Vs1, V(t) -> Vs0, K(t+2) -> Ks0, V(t+1) -> Vs1
+        iteration(t, Ks0, Ks1, Vs1, Vs0, Ks0, Vs1);
+        if (t + 1 > ntiles) break;
+        iteration(t + 1, Ks1, Ks0, Vs0, Vs1, Ks1, Vs0);
     }
+    if (grp == 0) __syncthreads();  // matches group B's offset barrier
 
     // Epilogue: lanes l and l^32 hold halves of the row sums.
     const float lt = pair_sum(l_run);
@@ -364,11 +440,11 @@ hipError_t launch_d(const PrefillArgs& a, hipStream_t stream) {
     const dim3 grid((unsigned)nqb * a.B * a.Hkv);
     const float c1 = (float)((double)a.scale * 1.4426950408889634);
     if (c1 > 0.f) {
-        hipLaunchKernelGGL((prefill_bf16_kernel<D, true>), grid, dim3(256), 0, stream, (const bf16*)a.q,
+        hipLaunchKernelGGL((prefill_bf16_kernel<D, true>), grid, dim3(512), 0, stream, (const bf16*)a.q,
                            (const bf16*)a.k, (const bf16*)a.v, (bf16*)a.out, a.lse, a.B, a.Hq, a.Hkv, a.T, G, BMt,
                            nqb, c1);
     } else {
-        hipLaunchKernelGGL((prefill_bf16_kernel<D, false>), grid, dim3(256), 0, stream, (const bf16*)a.q,
+        hipLaunchKernelGGL((prefill_bf16_kernel<D, false>), grid, dim3(512), 0, stream, (const bf16*)a.q,
                            (const bf16*)a.k, (const bf16*)a.v, (bf16*)a.out, a.lse, a.B, a.Hq, a.Hkv, a.T, G, BMt,
                            nqb, c1);
     }
