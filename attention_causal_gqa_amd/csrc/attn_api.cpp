@@ -37,7 +37,7 @@ int from_hip(hipError_t e, const char* what) {
 }
 
 constexpr int kPageSize = 16;
-constexpr int kMaxDecodeGroup = 8;
+constexpr int kMaxDecodeGroup = 16;
 constexpr int kMaxPrefillGroup = 128;
 constexpr int64_t kMaxGrid = 0x7fffffff;
 

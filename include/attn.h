@@ -56,7 +56,7 @@ extern "C" {
 typedef enum attn_status {
     ATTN_OK = 0,
     ATTN_ERR_INVALID_ARG = -1, /* null pointer, bad size, misaligned, Hq % Hkv != 0, ... */
-    ATTN_ERR_UNSUPPORTED = -2, /* valid request this build has no kernel for (dtype, d, page size) */
+    ATTN_ERR_UNSUPPORTED = -2, /* valid request this build has no kernel for (dtype, d, page size, group) */
     ATTN_ERR_WORKSPACE = -3,   /* workspace null or smaller than attn_decode_workspace_bytes() */
     ATTN_ERR_HIP = -4          /* the HIP runtime reported an error while enqueuing */
 } attn_status_t;
@@ -121,7 +121,7 @@ size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int d, int page_size,
  *   num_splits     : as for attn_decode_num_splits (0 = automatic)
  *   workspace      : device, at least attn_decode_workspace_bytes(...) bytes;
  *                    owned by the caller, contents on entry are ignored
- *   dtype          : ATTN_BF16; d = 128 or 64; page_size = 16
+ *   dtype          : ATTN_BF16; d = 128 or 64; page_size = 16; Hq / Hkv <= 16
  * Slots at or past seq_lens[b] may hold anything (NaN included): they are
  * never used.  The block table and seq_lens are read on the device only;
  * values outside the ranges above are undefined behaviour (check them with

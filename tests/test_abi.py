@@ -107,7 +107,7 @@ def decode(lib, q=FAKE, kp=FAKE, vp=FAKE, bt=FAKE, sl=FAKE, out=FAKE, lse=None, 
         (dict(dtype=0), A.ATTN_ERR_UNSUPPORTED),
         (dict(d=80), A.ATTN_ERR_UNSUPPORTED),
         (dict(ps=32), A.ATTN_ERR_UNSUPPORTED),
-        (dict(Hq=32, Hkv=2), A.ATTN_ERR_UNSUPPORTED),
+        (dict(Hq=34, Hkv=2), A.ATTN_ERR_UNSUPPORTED),
         (dict(ws=None), A.ATTN_ERR_WORKSPACE),
         (dict(wsb=16), A.ATTN_ERR_WORKSPACE),
     ],

@@ -74,7 +74,7 @@ def test_edge_lengths(num_splits):
     check(inp, synth.fp32_scale(128), f"edge lengths, splits={num_splits}", num_splits=num_splits)
 
 
-@pytest.mark.parametrize("Hq,Hkv,d", [(8, 8, 128), (6, 2, 128), (7, 1, 128), (16, 2, 128), (8, 2, 64), (4, 4, 64)])
+@pytest.mark.parametrize("Hq,Hkv,d", [(8, 8, 128), (6, 2, 128), (7, 1, 128), (16, 2, 128), (32, 2, 128), (8, 2, 64), (4, 4, 64), (16, 1, 64)])
 def test_group_sizes_and_d(Hq, Hkv, d):
     shp = synth.DecodeShape(5, Hq, Hkv, d, 16, 1, 700, torch.bfloat16)
     inp = synth.paged_inputs(shp, seed=Hq * 10 + Hkv + d, poison=float("nan"))
