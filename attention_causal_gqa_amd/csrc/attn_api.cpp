@@ -47,19 +47,26 @@ struct Plan {
     int pages_per_split;
 };
 
-// Automatic plan: the largest pages-per-split in {16, 8, 4} that still gives
-// at least 4096 workgroups (16 per CU on 256 CUs), so that sequences of very
-// different lengths even out across the chip; never fewer than 4 pages per
-// split, to keep partial-result traffic small next to the K/V stream.
+// A split is an item: pages_per_split (pps) consecutive pages of one
+// (sequence, kv head), starting at a multiple of pps.  The streaming kernel
+// hands each wave an equal share of all pages, cut only at item starts, so
+// a wave's share is off by at most pps - 1 pages; a sequence is cut into at
+// most `splits` pieces.
+//
+// Automatic plan: pps about 1/32 of the page count per wave when every
+// sequence is full (B * Hkv * W pages over 2048 waves, 8 per CU on 256
+// CUs), clamped to [1, 64].  The share imbalance then stays near 3%, and
+// the slot count ceil(W / pps) stays near 65536 / (B * Hkv), bounding the
+// workspace.
 Plan make_plan(int B, int Hkv, int W, int num_splits) {
     Plan p{};
     if (num_splits > 0) {
         const int s = num_splits < W ? num_splits : W;
         p.pages_per_split = (W + s - 1) / s;
     } else {
-        int pps = 16;
-        while (pps > 4 && (int64_t)B * Hkv * ((W + pps - 1) / pps) < 4096) pps /= 2;
-        p.pages_per_split = pps;
+        const int64_t per_wave = ((int64_t)B * Hkv * W + 2047) / 2048;
+        const int64_t pps = per_wave / 32;
+        p.pages_per_split = (int)(pps < 1 ? 1 : pps > 64 ? 64 : pps);
     }
     p.splits = (W + p.pages_per_split - 1) / p.pages_per_split;
     return p;
@@ -167,7 +174,7 @@ int attn_decode_paged(const void* q, const void* k_pages, const void* v_pages, c
         return fail(ATTN_ERR_INVALID_ARG, "block_table, seq_lens and lse must be 4-byte aligned");
 
     const Plan plan = make_plan(B, Hkv, max_pages_per_seq, num_splits);
-    if ((int64_t)plan.splits * Hkv * B > kMaxGrid) return fail(ATTN_ERR_INVALID_ARG, "problem too large");
+    if ((int64_t)B * Hq > kMaxGrid) return fail(ATTN_ERR_INVALID_ARG, "problem too large");
     const size_t need = workspace_for(B, Hq, d, plan);
     if (!workspace || workspace_bytes < need)
         return fail(ATTN_ERR_WORKSPACE, "workspace %zu bytes given, %zu needed", workspace ? workspace_bytes : 0, need);

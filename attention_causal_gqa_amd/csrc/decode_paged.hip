@@ -24,6 +24,8 @@
 // sequence's non-empty splits are merged with log-sum-exp weights
 // (block-wise softmax statistics, llm-from-scratch "Project Overview",
 // "Performance Layer: kernel/ and parallel/").
+#include <atomic>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -31,6 +33,7 @@ namespace attn {
 namespace {
 
 constexpr int kPage = 16;
+constexpr int kMaxDevices = 64;
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
@@ -46,22 +49,38 @@ __device__ __forceinline__ float row_pair_sum(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-__device__ __forceinline__ void dma16(const void* g, char* lds_base) {
-    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
-                                     (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
-}
-
 __device__ __forceinline__ u32x2 lds_read_tr16(const char* p) {
     typedef short v4i16 __attribute__((ext_vector_type(4)));
     v4i16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(p));
     return __builtin_bit_cast(u32x2, r);
 }
 
-// Wait until at most N vector-memory operations of this wave are in flight
-// (s_waitcnt vmcnt(N), other counters untouched; gfx9 encoding).
+// The page loop's global loads are issued from inline assembly, so the
+// compiler's wait-count insertion does not see them; left to it, it drains
+// every outstanding load (including the next page's) before the first MFMA
+// of each page.  Their completion is awaited explicitly with wait_loads.
+__device__ __forceinline__ u32x4 gload16(const void* p) {
+    u32x4 r;
+    asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(r) : "v"(p) : "memory");
+    return r;
+}
+// 16 bytes per lane, HBM -> LDS: lane l's bytes land at lds + 16 l (lds is
+// wave-uniform, passed in M0).
+__device__ __forceinline__ void dma16(const void* g, const char* lds) {
+    const uint32_t m = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)lds;
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(m) : "memory", "m0");
+}
+// Wait until at most N of this wave's vector-memory operations are in
+// flight (loads complete in issue order).  The memory clobber keeps LDS
+// reads below it; the empty statements that follow, one per register set,
+// keep the loaded registers' consumers below it.
 template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
+__device__ __forceinline__ void wait_loads() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+template <typename T>
+__device__ __forceinline__ void after_wait(T& r) {
+    asm volatile("" : "+v"(r));
 }
 
 // XOR swizzle of the 16-byte chunks of a V page row in LDS: chunk c of row
@@ -73,8 +92,39 @@ __device__ __forceinline__ int vswz(int r) {
     else return 2 * ((r >> 1) & 3);
 }
 
-// Split kernel.  Workgroup = 4 waves per (sequence, kv head, split); wave w
-// takes pages w, w+4, ... of the split.  Per page (16 tokens) and wave:
+// Position in a wave's stream of (sequence b, kv head, page j) triples, in
+// flattened order: sequence-major, then kv head, then page.  x is the
+// flattened offset; n and L are sequence b's page and token counts.
+struct Cursor {
+    int b, kvh, j, n, L;
+    long long x;
+};
+
+__device__ __forceinline__ int pages_of(int L) { return (L + kPage - 1) / kPage; }
+
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int t = __shfl_up(v, o);
+        if (lane >= o) v += t;
+    }
+    return v;
+}
+
+// Streaming split kernel: one wave per workgroup, as many workgroups as fit
+// on the chip at once.  The work is the flattened stream of all
+// (sequence, kv head, page) triples (Hkv * sum_b ceil(L_b / 16) pages); wave
+// w takes the pages from snap(w C) up to snap((w + 1) C), C = ceil(total /
+// waves), where snap moves an offset up to the next item start.  An item is
+// a run of pps pages of one (sequence, kv head) beginning at a multiple of
+// pps, so every wave gets C pages give or take pps, whatever the mix of
+// lengths, and a sequence's keys are cut only at item starts.
+//
+// A wave keeps one online softmax per (sequence, kv head) run it meets (a
+// piece) and writes it, normalised, with its log-sum-exp into the slot of
+// the piece's first item; the piece's other item slots get lse = -inf as
+// the wave reaches them, and the combine kernel skips those.  Per page (16 tokens) and wave:
 //   S^T = K Q^T   (16 tokens x 16 head columns; v_mfma_f32_16x16x32_bf16,
 //                  K read from HBM straight into the A-operand layout, the G
 //                  query heads of the kv group in the B columns, zero-padded)
@@ -82,14 +132,16 @@ __device__ __forceinline__ int vswz(int r) {
 //   O  += P V     (16 head rows x d; v_mfma_f32_16x16x16bf16_1k: the S^T
 //                  accumulator layout is exactly the P A-operand layout, V
 //                  comes HBM -> LDS by DMA and is read transposed)
-// The next page's K and V loads are in flight while a page is computed.
+// The next page's K and V loads are in flight while a page is computed, and
+// the block-table entry of the page after that is loaded a step earlier.
 template <int D>
-__global__ __launch_bounds__(256) void decode_split_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kp,
-                                                           const bf16* __restrict__ vp,
-                                                           const int32_t* __restrict__ block_table,
-                                                           const int32_t* __restrict__ seq_lens,
-                                                           float* __restrict__ o_part, float* __restrict__ lse_part,
-                                                           int Hq, int Hkv, int G, int W, int S, int pps, float c1) {
+__global__ __launch_bounds__(64) void decode_stream_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kp,
+                                                            const bf16* __restrict__ vp,
+                                                            const int32_t* __restrict__ block_table,
+                                                            const int32_t* __restrict__ seq_lens,
+                                                            float* __restrict__ o_part, float* __restrict__ lse_part,
+                                                            int B, int Hq, int Hkv, int G, int W, int S, int pps,
+                                                            float c1) {
     constexpr int NKK = D / 32;        // k-steps of QK^T (16x16x32)
     constexpr int NB = D / 16;         // 16-column blocks of O (16x16x16)
     constexpr int ROWB = D * 2;        // bytes per token row
@@ -97,56 +149,97 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const bf16* __restric
     constexpr int NDMA = SLICEB / 1024;   // wave-wide 1 KiB DMAs per slice
     constexpr int RPD = 1024 / ROWB;      // rows per DMA
     constexpr int CPR = D / 8;            // 16-byte chunks per row
-    // Per wave: two V slices (double buffer).  After the page loop a wave's
-    // region holds its partial O (16 head rows x D fp32 = 2 slices).
-    __shared__ __attribute__((aligned(1024))) char Vb0[4][SLICEB];
-    __shared__ __attribute__((aligned(1024))) char Vb1[4][SLICEB];
-    __shared__ float sM[4][16];
-    __shared__ float sL[4][16];
-    __shared__ float sLL[4][16];
+    // Two V slices (double buffer).
+    __shared__ __attribute__((aligned(1024))) char Vb0[SLICEB];
+    __shared__ __attribute__((aligned(1024))) char Vb1[SLICEB];
 
-    const int s = blockIdx.x % S;
-    const int bk = blockIdx.x / S;
-    const int kvh = bk % Hkv;
-    const int b = bk / Hkv;
-
-    const int L = seq_lens[b];
-    const int npages = (L + kPage - 1) / kPage;
-    const int p0 = s * pps;
-    const int p1 = min(p0 + pps, npages);
-    if (p0 >= p1) return;  // empty split: the combine kernel never reads it
-
-    const int tid = threadIdx.x;
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int lane = tid & 63;
+    const int lane = threadIdx.x;
     const int hd = lane & 15;  // head column (S^T, P) / d within a 16-block (O)
     const int g = lane >> 4;   // 16-lane row: tokens 4g..4g+3 (S^T, P) / head rows 4g..4g+3 (O)
 
-    // Q^T as the B operand of S^T: lane holds Q[head hd][32kk + 8g .. +7]; heads >= G are zero.
-    bf16x8 qb[NKK];
-#pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) {
-        if (hd < G) {
-            qb[kk] = *reinterpret_cast<const bf16x8*>(q + ((size_t)b * Hq + kvh * G + hd) * D + 32 * kk + 8 * g);
-        } else {
-#pragma unroll
-            for (int j = 0; j < 8; ++j) qb[kk][j] = (bf16)0.f;
-        }
+    // ---- this wave's share of the page stream
+    long long total = 0;
+    for (int c0 = 0; c0 < B; c0 += 64) {
+        const int bb = c0 + lane;
+        const int n = bb < B ? pages_of(seq_lens[bb]) : 0;
+        total += __builtin_amdgcn_readlane(wave_incl_scan(n, lane), 63);
     }
+    total *= Hkv;
+    const long long C = (total + gridDim.x - 1) / gridDim.x;
+    const long long xa = (long long)blockIdx.x * C;
+    if (xa >= total) return;
+    const long long xb = xa + C < total ? xa + C : total;
 
-    // Page ids of the split, 64 at a time, one per lane; a wave visits its
-    // pages in increasing order, so each chunk is loaded once.
-    const int32_t* bt_row = block_table + (size_t)b * W + p0;
-    int pid_chunk = -1;
-    int my_pid = 0;
-    auto page_id = [&](int p) __attribute__((always_inline)) {
-        const int j = p - p0;  // wave-uniform
-        if ((j >> 6) != pid_chunk) {
-            pid_chunk = j >> 6;
-            const int jj = (pid_chunk << 6) + lane;
-            my_pid = (jj < p1 - p0) ? bt_row[jj] : 0;
+    // Cursor at snap(x), x < total; c.j may equal c.n (then the item start
+    // is the next run's first page, see normalize).
+    auto locate = [&](long long x, Cursor& c) __attribute__((always_inline)) {
+        long long carry = 0;  // pages of the sequences before this chunk
+        for (int c0 = 0; c0 < B; c0 += 64) {
+            const int bb = c0 + lane;
+            const int Lb = bb < B ? seq_lens[bb] : 0;
+            const int n = pages_of(Lb);
+            const int incl = wave_incl_scan(n, lane);
+            const long long e = (carry + incl - n) * Hkv;  // flattened offset of sequence bb
+            const unsigned long long hit = __ballot(n > 0 && e <= x && x < e + (long long)n * Hkv);
+            if (hit) {
+                const int src = __builtin_ctzll(hit);
+                c.b = c0 + src;
+                c.n = __builtin_amdgcn_readlane(n, src);
+                c.L = __builtin_amdgcn_readlane(Lb, src);
+                const long long eb = (carry + __builtin_amdgcn_readlane(incl, src) - c.n) * Hkv;
+                const int r = (int)(x - eb);
+                c.kvh = r / c.n;
+                const int jr = (r % c.n + pps - 1) / pps * pps;
+                c.j = jr < c.n ? jr : c.n;
+                c.x = eb + (long long)c.kvh * c.n + c.j;
+                return;
+            }
+            carry += __builtin_amdgcn_readlane(incl, 63);
         }
-        return __builtin_amdgcn_readlane(my_pid, j & 63);
+    };
+    // Move a cursor with j == n to the next run's first page.  Only called
+    // when c.x < total, so a non-empty sequence follows.
+    auto normalize = [&](Cursor& c) __attribute__((always_inline)) {
+        if (c.j < c.n) return;
+        c.j = 0;
+        if (++c.kvh < Hkv) return;
+        c.kvh = 0;
+        do {
+            ++c.b;
+            c.L = seq_lens[c.b];
+            c.n = pages_of(c.L);
+        } while (c.n == 0);
+    };
+
+    Cursor cc;  // page being computed
+    locate(xa, cc);
+    long long xe = total;
+    if (xb < total) {
+        Cursor ce;
+        locate(xb, ce);
+        xe = ce.x;
+    }
+    const long long xs = cc.x;
+    if (xs >= xe) return;  // no item starts in this wave's range
+    normalize(cc);
+
+    auto advance = [&](Cursor& c) __attribute__((always_inline)) {
+        ++c.x;
+        ++c.j;
+        if (c.x < xe) normalize(c);
+    };
+    auto page_id = [&](const Cursor& c) __attribute__((always_inline)) {
+        return block_table[(size_t)c.b * W + c.j];
+    };
+
+    // Q^T as the B operand of S^T: lane holds Q[head hd][32kk + 8g .. +7].
+    // Columns hd >= G repeat head G - 1; their results are never stored.
+    bf16x8 qb[NKK];
+    auto load_q = [&](int b, int kvh) __attribute__((always_inline)) {
+        const int hh = hd < G ? hd : G - 1;
+        const bf16* qrow = q + ((size_t)b * Hq + (size_t)kvh * G + hh) * D + 8 * g;
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) qb[kk] = __builtin_bit_cast(bf16x8, gload16(qrow + 32 * kk));
     };
 
     // K A-operand: lane holds K[token hd][32kk + 8g .. +7].
@@ -165,29 +258,31 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const bf16* __restric
     const int vrow = 4 * g + (vi >> 2);
     const int vread = vrow * ROWB + 8 * (vi & 1) + ((((vi & 3) >> 1) ^ vswz<D>(vrow)) << 4);
 
-    auto issue_page = [&](int p, char* vdst, u32x4 (&ka)[NKK]) __attribute__((always_inline)) {
-        const int pid = page_id(p);
+    auto issue_page = [&](int pid, int kvh, char* vdst, u32x4(&ka)[NKK]) __attribute__((always_inline)) {
         const size_t slice = ((size_t)pid * Hkv + kvh) * (kPage * D);
         const char* kb = reinterpret_cast<const char*>(kp + slice);
 #pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) ka[kk] = *reinterpret_cast<const u32x4*>(kb + koff + 64 * kk);
+        for (int kk = 0; kk < NKK; ++kk) ka[kk] = gload16(kb + koff + 64 * kk);
         const char* vb = reinterpret_cast<const char*>(vp + slice);
 #pragma unroll
         for (int n = 0; n < NDMA; ++n) dma16(vb + voff[n], vdst + 1024 * n);
     };
 
     f32x4 oacc[NB];
+    float m_run, l_run, l_lse;  // running max (base-2 scaled), sum(bf16(p)), sum(p)
+    auto reset = [&]() __attribute__((always_inline)) {
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) oacc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m_run = -INFINITY;  // running max of head column hd, base-2 scaled
-    float l_run = 0.f;        // this lane's share of sum(bf16(p)) (its tokens)
-    float l_lse = 0.f;        // the same over fp32 p
+        for (int nb = 0; nb < NB; ++nb) oacc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        m_run = -INFINITY;
+        l_run = 0.f;
+        l_lse = 0.f;
+    };
     constexpr uint32_t kOnes = 0x3F803F80u;
 
-    auto compute_page = [&](int p, const u32x4 (&kcur)[NKK], char* vbuf) __attribute__((always_inline)) {
+    auto compute_page = [&](const Cursor& c, const u32x4(&kcur)[NKK], char* vbuf) __attribute__((always_inline)) {
         // Tokens past L in the last page: zero their V rows (the pool may
         // hold NaN there, and 0 * NaN would reach O).
-        const int nvalid = L - p * kPage;
+        const int nvalid = c.L - c.j * kPage;
         if (nvalid < kPage) {
 #pragma unroll
             for (int n = 0; n < NDMA; ++n) {
@@ -209,8 +304,8 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const bf16* __restric
         mx = pair_max(mx);  // page max of head column hd, in all 4 rows
         // Move the running max only when the page max exceeds it by more
         // than 8 (base 2): probabilities stay below 256 and O is rescaled
-        // rarely.  The first page always moves it (m_run = -inf); a page
-        // always has a valid token, so mx is finite.
+        // rarely.  A piece's first page always moves it (m_run = -inf); a
+        // page always has a valid token, so mx is finite.
         const bool grow = mx > m_run + 8.f;
         if (__any(grow)) {
             const float mn = grow ? mx : m_run;
@@ -234,7 +329,6 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const bf16* __restric
         l_run = dot2_bf16(p23, kOnes, dot2_bf16(p01, kOnes, l_run));
         l_lse += (pr[0] + pr[1]) + (pr[2] + pr[3]);
         const u32x2 pa = {p01, p23};  // A operand: P[head hd][tokens 4g .. 4g+3]
-        // V must have landed (this page's DMA is older than the next page's).
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
             const u32x2 vb = lds_read_tr16(vbuf + (vread ^ (nb << 5)));
@@ -243,131 +337,212 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const bf16* __restric
         }
     };
 
+    // Current piece: its (sequence, kv head) and first item slot.
+    int pb = 0, pkvh = 0, ps0 = 0;
+    auto flush = [&]() __attribute__((always_inline)) {
+        // Row sums: add the four 16-lane rows (tokens 4g..4g+3).
+        const float lr = pair_sum(row_pair_sum(l_run));
+        const float ll = pair_sum(row_pair_sum(l_lse));
+        const float inv = 1.f / lr;
+        const size_t bh0 = (size_t)pb * Hq + (size_t)pkvh * G;
+        // lane holds O[head 4g + i][16nb + hd]
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int head = 4 * g + i;
+            const float ih = __shfl(inv, head);
+            if (head < G) {
+                float* dst = o_part + ((bh0 + head) * S + ps0) * D + hd;
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) dst[16 * nb] = oacc[nb][i] * ih;
+            }
+        }
+        if (g == 0 && hd < G) lse_part[(bh0 + hd) * S + ps0] = (m_run + log2f(ll)) * kLn2;
+    };
+
     // Page loop, unrolled by two over two (K registers, V buffer) sets: the
     // next page's loads go into the other set while this page is computed.
     // The V buffers are distinct arrays, so the compiler does not make LDS
     // reads wait for the other buffer's DMA.
-    char* vbuf0 = Vb0[w];
-    char* vbuf1 = Vb1[w];
     u32x4 ka0[NKK], ka1[NKK];
-    int p = p0 + w;
-    if (p < p1) issue_page(p, vbuf0, ka0);
-    while (p < p1) {
-        if (p + 4 < p1) {
-            issue_page(p + 4, vbuf1, ka1);
-            wait_vmcnt<NKK + NDMA>();
-        } else {
-            wait_vmcnt<0>();
-        }
-        compute_page(p, ka0, vbuf0);
-        p += 4;
-        if (p >= p1) break;
-        if (p + 4 < p1) {
-            issue_page(p + 4, vbuf0, ka0);
-            wait_vmcnt<NKK + NDMA>();
-        } else {
-            wait_vmcnt<0>();
-        }
-        compute_page(p, ka1, vbuf1);
-        p += 4;
-    }
+    issue_page(page_id(cc), cc.kvh, Vb0, ka0);
+    Cursor cf = cc;  // page whose loads go out next
+    advance(cf);
+    int pid_f = cf.x < xe ? page_id(cf) : 0;
 
-    // Row sums of this wave: add the four 16-lane rows (tokens 4g..4g+3).
-    l_run = pair_sum(row_pair_sum(l_run));
-    l_lse = pair_sum(row_pair_sum(l_lse));
-    if (g == 0) {
-        sM[w][hd] = m_run;
-        sL[w][hd] = l_run;
-        sLL[w][hd] = l_lse;
-    }
-    // Partial O into this wave's own LDS region (its V buffers, no longer read):
-    // lane holds O[head 4g + i][16nb + hd].
-    float* sO = reinterpret_cast<float*>(Vb0[w]);  // 16 x D floats span Vb0[w] and Vb1[w]
-    static_assert(sizeof(Vb0[0]) * 2 >= 16 * D * sizeof(float), "partial O must fit the wave's V buffers");
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int idx = (4 * g + i) * D + 16 * nb + hd;
-            float* dst = idx < SLICEB / 4 ? sO + idx : reinterpret_cast<float*>(Vb1[w]) + (idx - SLICEB / 4);
-            *dst = oacc[nb][i];
+    auto step = [&](u32x4(&kx)[NKK], char* bx, u32x4(&ky)[NKK], char* by) __attribute__((always_inline)) {
+        const bool first_of_run = cc.j == 0 || cc.x == xs;
+        if (first_of_run) load_q(cc.b, cc.kvh);
+        const bool more = cf.x < xe;
+        Cursor cn = cf;
+        int pid_n = 0;
+        if (more) {
+            issue_page(pid_f, cf.kvh, by, ky);
+            advance(cn);
+            if (cn.x < xe) pid_n = page_id(cn);
+            wait_loads<NKK + NDMA>();  // all but the next page's loads
+        } else {
+            wait_loads<0>();
         }
-    __syncthreads();
-
-    // Merge the 4 waves (a wave with no page has m = -inf, l = 0); write
-    // the normalised partial output and its LSE.
-    for (int idx = tid; idx < G * D; idx += 256) {
-        const int h = idx / D;
-        const int d = idx % D;
-        float M = sM[0][h];
 #pragma unroll
-        for (int ww = 1; ww < 4; ++ww) M = fmaxf(M, sM[ww][h]);
-        float lsum = 0.f, llse = 0.f, osum = 0.f;
-#pragma unroll
-        for (int ww = 0; ww < 4; ++ww) {
-            const float f = (sM[ww][h] == -INFINITY) ? 0.f : fast_exp2(sM[ww][h] - M);
-            const int oi = h * D + d;
-            const float ov = oi < SLICEB / 4 ? reinterpret_cast<const float*>(Vb0[ww])[oi]
-                                             : reinterpret_cast<const float*>(Vb1[ww])[oi - SLICEB / 4];
-            lsum = fmaf(f, sL[ww][h], lsum);
-            llse = fmaf(f, sLL[ww][h], llse);
-            osum = fmaf(f, ov, osum);
+        for (int kk = 0; kk < NKK; ++kk) {
+            after_wait(kx[kk]);
+            after_wait(qb[kk]);
         }
-        const size_t bh = (size_t)b * Hq + kvh * G + h;
-        o_part[(bh * S + s) * D + d] = osum / lsum;
-        if (d == 0) lse_part[bh * S + s] = (M + log2f(llse)) * kLn2;
+        if (first_of_run) {
+            if (cc.x != xs) flush();
+            reset();
+            pb = cc.b;
+            pkvh = cc.kvh;
+            ps0 = cc.j / pps;
+        } else if (cc.j % pps == 0 && lane < G) {
+            // a later item of the piece: mark its slot (one store per page
+            // at most, so the loads in flight stay countable)
+            lse_part[((size_t)pb * Hq + (size_t)pkvh * G + lane) * S + cc.j / pps] = -INFINITY;
+        }
+        compute_page(cc, kx, bx);
+        cc = cf;
+        cf = cn;
+        pid_f = pid_n;
+        return more;
+    };
+    for (;;) {
+        if (!step(ka0, Vb0, ka1, Vb1)) break;
+        if (!step(ka1, Vb1, ka0, Vb0)) break;
     }
+    flush();
 }
 
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+    return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+    return x;
+}
+
+// Combine kernel: one wave per (sequence, query head).  The sequence's item
+// slots hold either a piece's normalised partial output and log-sum-exp or
+// lse = -inf (an item that continues a piece; its o_part is never written).
+// Pieces are merged with weights exp(lse_i - max lse) (block-wise softmax
+// statistics, llm-from-scratch "Project Overview", "Performance Layer:
+// kernel/ and parallel/").  Slot lse values are read 64 at a time, one per
+// lane; the pieces among them are found by ballot and their partial rows
+// are loaded eight at a time, so the loads overlap.
 template <int D>
-__global__ __launch_bounds__(D) void decode_combine_kernel(const float* __restrict__ o_part,
-                                                           const float* __restrict__ lse_part,
-                                                           const int32_t* __restrict__ seq_lens, bf16* __restrict__ out,
-                                                           float* __restrict__ lse, int Hq, int S, int pps) {
+__global__ __launch_bounds__(64) void decode_combine_kernel(const float* __restrict__ o_part,
+                                                            const float* __restrict__ lse_part,
+                                                            const int32_t* __restrict__ seq_lens,
+                                                            bf16* __restrict__ out, float* __restrict__ lse, int Hq,
+                                                            int S, int pps) {
+    constexpr int NDW = D / 64;  // d values per lane
+    constexpr int BATCH = 8;
     const int bh = blockIdx.x;
     const int b = bh / Hq;
-    const int d = threadIdx.x;
+    const int lane = threadIdx.x;
     const int L = seq_lens[b];
+    bf16* orow = out + (size_t)bh * D;
     if (L == 0) {
-        out[(size_t)bh * D + d] = (bf16)0.f;
-        if (lse != nullptr && d == 0) lse[bh] = -INFINITY;
+#pragma unroll
+        for (int k = 0; k < NDW; ++k) orow[64 * k + lane] = (bf16)0.f;
+        if (lse != nullptr && lane == 0) lse[bh] = -INFINITY;
         return;
     }
     const int ns = ((L + kPage - 1) / kPage + pps - 1) / pps;
     const float* lp = lse_part + (size_t)bh * S;
+    const float* op = o_part + (size_t)bh * S * D;
     float M = -INFINITY;
-    for (int s = 0; s < ns; ++s) M = fmaxf(M, lp[s]);
-    float wsum = 0.f, acc = 0.f;
-    for (int s = 0; s < ns; ++s) {
-        const float wgt = fast_exp2((lp[s] - M) * kLog2e);
-        wsum += wgt;
-        acc = fmaf(wgt, o_part[((size_t)bh * S + s) * D + d], acc);
+    for (int c0 = 0; c0 < ns; c0 += 64) {
+        const int s = c0 + lane;
+        if (s < ns) M = fmaxf(M, lp[s]);
     }
-    out[(size_t)bh * D + d] = (bf16)(acc / wsum);
-    if (lse != nullptr && d == 0) lse[bh] = M + logf(wsum);
+    M = wave_max(M);  // finite: slot 0 always starts a piece
+    float acc[NDW];
+#pragma unroll
+    for (int k = 0; k < NDW; ++k) acc[k] = 0.f;
+    float wsum = 0.f;
+    for (int c0 = 0; c0 < ns; c0 += 64) {
+        const int s = c0 + lane;
+        const float l = s < ns ? lp[s] : -INFINITY;
+        const float wt = fast_exp2((l - M) * kLog2e);  // 0 for non-pieces
+        wsum += wt;
+        unsigned long long mask = __ballot(l != -INFINITY);
+        const int first = mask ? __builtin_ctzll(mask) : 0;
+        while (mask) {
+            int js[BATCH];
+            float ws[BATCH];
+#pragma unroll
+            for (int u = 0; u < BATCH; ++u) {
+                if (mask) {
+                    js[u] = __builtin_ctzll(mask);
+                    mask &= mask - 1;
+                    ws[u] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wt), js[u]));
+                } else {
+                    js[u] = first;  // a written slot, weighted 0
+                    ws[u] = 0.f;
+                }
+            }
+            float v[BATCH][NDW];
+#pragma unroll
+            for (int u = 0; u < BATCH; ++u)
+#pragma unroll
+                for (int k = 0; k < NDW; ++k) v[u][k] = op[(size_t)(c0 + js[u]) * D + 64 * k + lane];
+#pragma unroll
+            for (int u = 0; u < BATCH; ++u)
+#pragma unroll
+                for (int k = 0; k < NDW; ++k) acc[k] = fmaf(ws[u], v[u][k], acc[k]);
+        }
+    }
+    wsum = wave_sum(wsum);
+    const float inv = 1.f / wsum;
+#pragma unroll
+    for (int k = 0; k < NDW; ++k) orow[64 * k + lane] = (bf16)(acc[k] * inv);
+    if (lse != nullptr && lane == 0) lse[bh] = M + logf(wsum);
+}
+
+// Workgroups of the streaming kernel that are resident at once on the
+// current device (compute units x occupancy), found once per device.
+template <int D>
+hipError_t stream_waves(int* nw) {
+    static std::atomic<int> cache[kMaxDevices];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    int v = cache[dev].load(std::memory_order_relaxed);
+    if (v == 0) {
+        int cus = 0, per = 0;
+        if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
+        if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, decode_stream_kernel<D>, 64, 0)) != hipSuccess)
+            return e;
+        v = cus * (per > 0 ? per : 1);
+        cache[dev].store(v, std::memory_order_relaxed);
+    }
+    *nw = v;
+    return hipSuccess;
 }
 
 template <int D>
-void launch_split(const DecodeArgs& a, hipStream_t stream, float c1) {
-    const dim3 grid((unsigned)a.num_splits * a.Hkv * a.B);
-    hipLaunchKernelGGL((decode_split_kernel<D>), grid, dim3(256), 0, stream, (const bf16*)a.q, (const bf16*)a.k_pages,
-                       (const bf16*)a.v_pages, a.block_table, a.seq_lens, a.o_part, a.lse_part, a.Hq, a.Hkv,
-                       a.Hq / a.Hkv, a.W, a.num_splits, a.pages_per_split, c1);
+hipError_t launch_split(const DecodeArgs& a, hipStream_t stream, float c1) {
+    int nw = 0;
+    const hipError_t e = stream_waves<D>(&nw);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((decode_stream_kernel<D>), dim3((unsigned)nw), dim3(64), 0, stream, (const bf16*)a.q,
+                       (const bf16*)a.k_pages, (const bf16*)a.v_pages, a.block_table, a.seq_lens, a.o_part, a.lse_part,
+                       a.B, a.Hq, a.Hkv, a.Hq / a.Hkv, a.W, a.num_splits, a.pages_per_split, c1);
+    return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream) {
     const float c1 = (float)((double)a.scale * 1.4426950408889634);
-    if (a.d == 128) {
-        launch_split<128>(a, stream, c1);
-    } else {
-        launch_split<64>(a, stream, c1);
-    }
-    hipError_t e = hipGetLastError();
+    const hipError_t e = a.d == 128 ? launch_split<128>(a, stream, c1) : launch_split<64>(a, stream, c1);
     if (e != hipSuccess) return e;
     if (a.d == 128) {
-        hipLaunchKernelGGL(decode_combine_kernel<128>, dim3((unsigned)a.B * a.Hq), dim3(128), 0, stream, a.o_part,
+        hipLaunchKernelGGL(decode_combine_kernel<128>, dim3((unsigned)a.B * a.Hq), dim3(64), 0, stream, a.o_part,
                            a.lse_part, a.seq_lens, (bf16*)a.out, a.lse, a.Hq, a.num_splits, a.pages_per_split);
     } else {
         hipLaunchKernelGGL(decode_combine_kernel<64>, dim3((unsigned)a.B * a.Hq), dim3(64), 0, stream, a.o_part,

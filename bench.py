@@ -202,7 +202,7 @@ def main():
         at_peak += nbytes / PEAK_HBM_BYTES
         parts["decode"] = {"ms": round(ms["decode"], 4), "ms_min": round(min(per["decode"]), 4),
                            "gbps": round(nbytes / t / 1e9, 1), "frac_of_peak": round(nbytes / t / PEAK_HBM_BYTES, 4),
-                           "bytes_per_launch": nbytes, "kernels": "split + combine",
+                           "bytes_per_launch": nbytes, "kernels": "stream + combine",
                            "num_splits": A.attn_decode_num_splits(dec_shape.B, dec_shape.Hq, dec_shape.Hkv,
                                                                   dec_shape.d, dec_shape.page_size,
                                                                   dec_inputs.max_pages_per_seq, 0)}
@@ -218,10 +218,10 @@ def main():
                 "traffic": measured_traffic("prefill_bf16_kernel", src), "source_hash": src}
     else:
         src = kernel_source_hash(["decode_paged.hip", "device_common.h"])
-        roof = {"kernel": "decode_split_kernel+decode_combine_kernel", "bound": "hbm",
+        roof = {"kernel": "decode_stream_kernel+decode_combine_kernel", "bound": "hbm",
                 "achieved": parts["decode"]["gbps"], "peak": PEAK_HBM_BYTES / 1e9, "unit": "GB/s",
                 "frac": round(parts["decode"]["gbps"] * 1e9 / PEAK_HBM_BYTES, 4),
-                "traffic": measured_traffic("decode_split_kernel", src), "source_hash": src}
+                "traffic": measured_traffic("decode_stream_kernel", src), "source_hash": src}
 
     cfg = {"workload": synth.WORKLOAD_NAMES[args.workload], "seed_prefill": args.workload,
            "seed_decode": 100 + args.workload}
