@@ -7,23 +7,20 @@
 // KV-cache decode with BF16 storage and FP32 accumulation of the
 // microLLM-rocm README, "Why this project exists").
 //
-// Split kernel: one workgroup (4 waves) per (sequence, kv head, split); a
-// split is a fixed run of pages_per_split pages of the sequence's page list,
-// and splits past the sequence's last page exit at once.  Wave w takes pages
-// w, w+4, ... of the split.  Each lane holds one 16-byte chunk (8 values of
-// d) of TPL tokens per page, so every K/V load is a coalesced 16-byte vector
-// load and a token row is read by CPR = d/8 consecutive lanes.  All G query
-// heads of the kv group are handled together, so each K/V byte is read once
-// for the whole group.  q.k partial sums use v_dot2 on bf16 pairs and a DPP
-// row reduction.  Every group of CPR lanes runs its own online softmax over
-// its tokens (no cross-lane max per page); the streams are merged once at
-// the end (shuffles within the wave, LDS across waves) into a normalised
-// partial output and its log-sum-exp, written to the workspace.
+// Streaming split kernel: as many one-wave workgroups as fit on the chip at
+// once, each taking an equal share of the flattened stream of all
+// (sequence, kv head, page) triples, so that sequences of any mix of lengths
+// keep every CU busy without a workgroup per split.  All G query heads of a
+// kv group are handled together (16x16 MFMA tiles, G columns used), so each
+// K/V byte is read once for the whole group.  Each run of pages of one
+// (sequence, kv head) that a wave meets is one piece; its normalised partial
+// output and log-sum-exp go to the workspace slot of the piece's first item
+// (a fixed run of pages_per_split pages).
 //
-// Combine kernel: per (sequence, query head), partial results of the
-// sequence's non-empty splits are merged with log-sum-exp weights
-// (block-wise softmax statistics, llm-from-scratch "Project Overview",
-// "Performance Layer: kernel/ and parallel/").
+// Combine kernel: per (sequence, query head), the pieces' partial results are
+// merged with log-sum-exp weights (block-wise softmax statistics,
+// llm-from-scratch "Project Overview", "Performance Layer: kernel/ and
+// parallel/").
 #include <atomic>
 
 #include "device_common.h"
@@ -158,11 +155,22 @@ __global__ __launch_bounds__(64) void decode_stream_kernel(const bf16* __restric
     const int g = lane >> 4;   // 16-lane row: tokens 4g..4g+3 (S^T, P) / head rows 4g..4g+3 (O)
 
     // ---- this wave's share of the page stream
+    // Sequences are taken 64 at a time, one per lane: token count, page
+    // count and inclusive prefix of page counts.  The first 64 stay in
+    // registers (with B <= 64 nothing is read twice).
+    int L0 = 0, n0 = 0, i0 = 0;
     long long total = 0;
     for (int c0 = 0; c0 < B; c0 += 64) {
         const int bb = c0 + lane;
-        const int n = bb < B ? pages_of(seq_lens[bb]) : 0;
-        total += __builtin_amdgcn_readlane(wave_incl_scan(n, lane), 63);
+        const int Lb = bb < B ? seq_lens[bb] : 0;
+        const int n = pages_of(Lb);
+        const int incl = wave_incl_scan(n, lane);
+        if (c0 == 0) {
+            L0 = Lb;
+            n0 = n;
+            i0 = incl;
+        }
+        total += __builtin_amdgcn_readlane(incl, 63);
     }
     total *= Hkv;
     const long long C = (total + gridDim.x - 1) / gridDim.x;
@@ -175,11 +183,14 @@ __global__ __launch_bounds__(64) void decode_stream_kernel(const bf16* __restric
     auto locate = [&](long long x, Cursor& c) __attribute__((always_inline)) {
         long long carry = 0;  // pages of the sequences before this chunk
         for (int c0 = 0; c0 < B; c0 += 64) {
-            const int bb = c0 + lane;
-            const int Lb = bb < B ? seq_lens[bb] : 0;
-            const int n = pages_of(Lb);
-            const int incl = wave_incl_scan(n, lane);
-            const long long e = (carry + incl - n) * Hkv;  // flattened offset of sequence bb
+            int Lb = L0, n = n0, incl = i0;
+            if (c0 != 0) {
+                const int bb = c0 + lane;
+                Lb = bb < B ? seq_lens[bb] : 0;
+                n = pages_of(Lb);
+                incl = wave_incl_scan(n, lane);
+            }
+            const long long e = (carry + incl - n) * Hkv;  // flattened offset of sequence c0 + lane
             const unsigned long long hit = __ballot(n > 0 && e <= x && x < e + (long long)n * Hkv);
             if (hit) {
                 const int src = __builtin_ctzll(hit);

@@ -7,23 +7,23 @@
 // accumulation as named in the microLLM-rocm README ("Why this project
 // exists").
 //
-// Work decomposition (one workgroup = 4 waves = 256 threads):
-//   * A workgroup owns 128 query rows of one (batch, kv head).  The rows are
-//     (token, head) pairs: BMt = floor(128 / G) consecutive tokens times the
+// Work decomposition (one workgroup = 8 waves = 512 threads, one per CU):
+//   * A workgroup owns 256 query rows of one (batch, kv head).  The rows are
+//     (token, head) pairs: BMt = floor(256 / G) consecutive tokens times the
 //     G query heads that share the kv head, so every K/V tile staged in LDS
 //     serves all G heads (GQA packing).  Wave w owns rows 32w .. 32w+31.
 //   * Keys are visited in tiles of 64, from key 0 up to the workgroup's last
 //     token; only the tiles that reach past the first token need the causal
-//     mask, applied per element.
+//     mask, applied per element behind a wave-uniform branch.
 //   * Scores are computed transposed, S^T = K Q^T, with
 //     v_mfma_f32_32x32x16_bf16 (A = K from LDS, B = Q^T held in registers):
 //     in the 32x32 accumulator layout each lane then holds 16 keys of one
 //     query column and lane l ^ 32 holds the other 16, so a row max or sum
-//     is 15 in-lane operations plus one v_permlane32_swap.
+//     is in-lane max3 / add operations plus one v_permlane32_swap.
 //   * The same accumulator registers, rounded to bf16, are exactly the B
 //     operand of O^T += V^T P^T (the contraction index is relabelled to the
 //     key order the accumulator layout gives).  V stays row-major in LDS; the
-//     A operand (V^T) comes from two transposing ds_read_b64_tr_b16 reads.
+//     A operand (V^T) comes from transposing ds_read_b64_tr_b16 reads.
 //   * K and V tiles are stored unpadded with an XOR swizzle of 16-byte
 //     chunks, so both operand read patterns are free of bank conflicts.
 //   * out is normalised by the sum of the same bf16-rounded probabilities
@@ -31,13 +31,14 @@
 //     V sum exactly to the normaliser; the log-sum-exp uses the fp32 sum.
 //   * The running max is only moved when a tile's max exceeds it by more
 //     than 8 (a factor 256 in base 2): rescaling O is then rare, and
-//     probabilities stay below 256, well inside fp32 and bf16 range.
+//     probabilities stay below 256, well inside fp32 and bf16 range.  The
+//     exponentials are computed against the old max before the decision and
+//     recomputed only on the rare tiles that move it.
 //   * K/V tiles go from HBM straight into LDS (global_load_lds_dwordx4, no
-//     staging registers), double-buffered: the next tile's DMA is in flight
-//     while the current tile is multiplied.  Two waves share each SIMD, so
-//     one wave's softmax overlaps the other's MFMAs.
-//   * The causal mask runs, behind a wave-uniform branch, only on the tiles
-//     that reach past the workgroup's first token.
+//     staging registers), double-buffered.  The 8 waves form two groups of 4
+//     that run in ping-pong (see below): on each SIMD one wave multiplies
+//     while the other computes its softmax, and the LDS operand reads of the
+//     next MFMAs are interleaved with the current ones by the scheduler.
 //   * Workgroups are launched heaviest first (last query blocks have the
 //     most keys); consecutive workgroup ids cycle over (batch, kv head) so a
 //     kv head's blocks fall on the same XCD and share its L2.

@@ -9,9 +9,14 @@ kernel.  Inputs are seeded synthetic tensors, resident in HBM before timing.
 Prints one JSON line.  ``value`` is the step's roofline fraction: the time the
 step's algorithmic work takes at MI355X peak (prefill flops at the bf16 MFMA
 peak plus decode bytes at the HBM peak) divided by the measured step time.
-Per-kernel rates come from HIP events recorded on the launch stream.
+``ms_per_step`` is host-clock time of K steps between two synchronizations.
+Per-kernel rates come from HIP events recorded on the launch stream around
+each part, in a second pass of K steps whose launches are queued while the
+GPU runs a short sleep kernel, so that the events time kernels rather than
+host launch latency.
 
     python bench.py [--steps K] [--warmup W] [--workload 5|3|4] [--no-cpu-baseline]
+    python bench.py --copy-calibration   # plain 1 GiB copy, reference for HBM byte counters
 """
 
 import argparse
@@ -46,25 +51,48 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--flush", action="store_true",
                    help="write a 512 MiB buffer before each step (outside the kernel events) to evict L2/MALL")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="only run a plain 1 GiB device-to-device copy ten times (reference for the HBM byte counters)")
     return p.parse_args()
 
 
+COPY_BYTES = 1 << 30
+
+
+def copy_calibration():
+    """A plain copy of known size: every launch reads and writes COPY_BYTES.  Profiling this run with
+    rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) gives the scale from counter bytes to HBM bytes."""
+    dev = torch.device("cuda:0")
+    src = torch.ones(COPY_BYTES, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(10):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration": {"bytes_read_per_launch": COPY_BYTES, "bytes_written_per_launch": COPY_BYTES,
+                                           "launches": 10}}), flush=True)
+
+
 def kernel_source_hash(names):
+    """Hash of the kernels' code (comments and blank lines removed, so that a comment edit keeps it)."""
     h = hashlib.sha256()
     for n in names:
-        with open(os.path.join(ROOT, "attention_causal_gqa_amd", "csrc", n), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "attention_causal_gqa_amd", "csrc", n)) as f:
+            for line in f:
+                code = line.split("//", 1)[0].rstrip()
+                if code:
+                    h.update(code.encode() + b"\n")
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kernel, src_hash):
+def measured_traffic(workload, kernel, src_hash):
     """HBM bytes per launch from the committed rocprofv3 --pmc summary, if it was taken on this source."""
     if not os.path.exists(PROFILE_COUNTERS):
         return None
     for line in open(PROFILE_COUNTERS):
         parts = line.split()
-        if len(parts) == 4 and parts[0] == "traffic" and parts[1] == kernel and parts[2] == src_hash:
-            return int(parts[3])
+        if len(parts) == 5 and parts[0] == "traffic" and parts[1] == str(workload) and parts[2] == kernel \
+                and parts[3] == src_hash:
+            return int(parts[4])
     return None
 
 
@@ -126,6 +154,9 @@ def main():
         print(json.dumps({"error": "this benchmark runs on one GPU only: the attention path has no multi-GPU "
                                    "code; run without --gpus or with --gpus 1"}))
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
     dev = torch.device("cuda:0")
     A.load_library()
     wl = synth.WORKLOADS[args.workload]
@@ -173,13 +204,25 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
+    # Timed region A (the step rate): K steps between two synchronizations,
+    # host clock.
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    # Timed region B (per-kernel times): the same K steps with HIP events
+    # around each part, on the launch stream.  A GPU-side sleep first lets
+    # the host queue all K steps, so the events time the kernels and not the
+    # host's marshalling and launch latency (which exceeds a short decode).
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    torch.cuda._sleep(200_000 * args.steps)
     for s in range(args.steps):
         step(evs[s])
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
 
     per = {n: [evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(args.steps)] for i, n in enumerate(names)}
     ms = {n: float(np.mean(per[n])) for n in names}
@@ -215,13 +258,14 @@ def main():
         roof = {"kernel": "prefill_bf16_kernel", "bound": "mfma", "achieved": parts["prefill"]["tflops"],
                 "peak": PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s",
                 "frac": round(parts["prefill"]["tflops"] * 1e12 / PEAK_BF16_FLOPS, 4),
-                "traffic": measured_traffic("prefill_bf16_kernel", src), "source_hash": src}
+                "traffic": measured_traffic(args.workload, "prefill_bf16_kernel", src), "source_hash": src}
     else:
         src = kernel_source_hash(["decode_paged.hip", "device_common.h"])
         roof = {"kernel": "decode_stream_kernel+decode_combine_kernel", "bound": "hbm",
                 "achieved": parts["decode"]["gbps"], "peak": PEAK_HBM_BYTES / 1e9, "unit": "GB/s",
                 "frac": round(parts["decode"]["gbps"] * 1e9 / PEAK_HBM_BYTES, 4),
-                "traffic": measured_traffic("decode_stream_kernel", src), "source_hash": src}
+                "traffic": measured_traffic(args.workload, "decode_stream_kernel+decode_combine_kernel", src),
+                "source_hash": src}
 
     cfg = {"workload": synth.WORKLOAD_NAMES[args.workload], "seed_prefill": args.workload,
            "seed_decode": 100 + args.workload}
