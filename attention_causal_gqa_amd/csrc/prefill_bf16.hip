@@ -80,10 +80,15 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const char* p) {
 
 // 16 bytes per lane from global memory straight into LDS (global_load_lds
 // dwordx4): lane l's data lands at lds_base + 16 l; lds_base must be the
-// same for the whole wave.
+// same for the whole wave (it goes in M0).  Issued from inline assembly: an
+// LDS DMA the compiler can see is counted as touching both global memory
+// and LDS, and while one is in flight the compiler makes every LDS read
+// wait for all earlier ones, which serialises the operand reads of the
+// MFMA phase.  Completion is awaited explicitly (s_waitcnt) before the
+// barrier that publishes the tile.
 __device__ __forceinline__ void dma16(const void* g, char* lds_base) {
-    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
-                                     (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
+    const uint32_t m = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds_base;
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(m) : "memory", "m0");
 }
 
 // Ping-pong schedule.  A workgroup is 8 waves = two groups of 4 (one wave
@@ -97,10 +102,11 @@ __device__ __forceinline__ void dma16(const void* g, char* lds_base) {
 // Barrier slots (slot s ends with the s-th barrier): group A runs phase 1 of
 // iteration t in slot 2t and phase 2 in slot 2t+1; group B one slot later.
 // K(t) and V(t-1) are read in slots 2t (A) and 2t+1 (B).  The DMA of K(t+1)
-// and V(t) is issued in slot 2t (group A at the start of its phase 1 of t,
-// group B at the start of its phase 2 of t-1, each for its own rows), into
-// the buffers last read in slots 2t-2 and 2t-1, and each wave waits for its
-// own DMA before the barrier that ends slot 2t+1.
+// and V(t) is issued in slot 2t by group A alone, at the end of its phase 1
+// of t (its MFMAs are shorter than group B's softmax, so the address unit
+// drains while A would otherwise wait at the barrier), into the buffers last
+// read in slots 2t-2 and 2t-1; A waits for it before the barrier that ends
+// slot 2t+1.
 template <int D, bool kPosScale>
 __global__ __launch_bounds__(512, 1) void prefill_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                                                               const bf16* __restrict__ v, bf16* __restrict__ out,
@@ -120,6 +126,12 @@ __global__ __launch_bounds__(512, 1) void prefill_bf16_kernel(const bf16* __rest
     __shared__ __attribute__((aligned(1024))) char Ks1[TILEB];
     __shared__ __attribute__((aligned(1024))) char Vs0[TILEB];
     __shared__ __attribute__((aligned(1024))) char Vs1[TILEB];
+
+    // Materialise every pointer argument now.  A scalar load still in flight
+    // (the lse pointer is otherwise first used after the key loop) makes the
+    // compiler wait for all LDS reads at every LDS wait inside the loop,
+    // because scalar loads can complete out of order.
+    __asm__ volatile("" ::"s"(q), "s"(k), "s"(v), "s"(out), "s"(lse));
 
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index 0..7, in an SGPR
@@ -157,11 +169,16 @@ __global__ __launch_bounds__(512, 1) void prefill_bf16_kernel(const bf16* __rest
     // Wave w owns DMAs w*NIW .. w*NIW + NIW-1 of every tile.
     const bf16* kbase = k + (size_t)(b * Hkv + kvh) * T * D;
     const bf16* vbase = v + (size_t)(b * Hkv + kvh) * T * D;
-    int drow[NIW];
-    uint32_t doff[NIW];  // byte offset of the lane's chunk within a tile of rows
+    // Group A (waves 0-3) issues every DMA: wave w takes the DMAs of wave
+    // slots w and w + 4, i.e. DMAs w*NIW .. and (w+4)*NIW .. of every tile.
+    constexpr int NDW = 2 * NIW;
+    int drow[NDW];
+    uint32_t doff[NDW];  // byte offset of the lane's chunk within a tile of rows
+    int dslot[NDW];      // wave-wide DMA index within the tile
 #pragma unroll
-    for (int j = 0; j < NIW; ++j) {
-        drow[j] = RPI * (w * NIW + j) + lane / CPR;
+    for (int j = 0; j < NDW; ++j) {
+        dslot[j] = ((w & 3) + 4 * (j / NIW)) * NIW + j % NIW;
+        drow[j] = RPI * dslot[j] + lane / CPR;
         doff[j] = (uint32_t)(drow[j] * ROWB + 16 * ((lane % CPR) ^ swz<CPR>(drow[j])));
     }
     // Keys past T are read as key T-1: they are masked for every stored row
@@ -170,13 +187,13 @@ __global__ __launch_bounds__(512, 1) void prefill_bf16_kernel(const bf16* __rest
         if (k0 + kBN <= T) {
             const char* tb = reinterpret_cast<const char*>(base + (size_t)k0 * D);
 #pragma unroll
-            for (int j = 0; j < NIW; ++j) dma16(tb + doff[j], dst + 1024 * (w * NIW + j));
+            for (int j = 0; j < NDW; ++j) dma16(tb + doff[j], dst + 1024 * dslot[j]);
         } else {
             const char* bb = reinterpret_cast<const char*>(base);
 #pragma unroll
-            for (int j = 0; j < NIW; ++j) {
+            for (int j = 0; j < NDW; ++j) {
                 const int key = min(k0 + drow[j], T - 1);
-                dma16(bb + (size_t)key * ROWB + (doff[j] - (uint32_t)(drow[j] * ROWB)), dst + 1024 * (w * NIW + j));
+                dma16(bb + (size_t)key * ROWB + (doff[j] - (uint32_t)(drow[j] * ROWB)), dst + 1024 * dslot[j]);
             }
         }
     };
@@ -374,43 +391,33 @@ __global__ __launch_bounds__(512, 1) void prefill_bf16_kernel(const bf16* __rest
         l_lse += (lsum[0] + lsum[1]) + (lsum[2] + lsum[3]);
     };
 
-    // Prologue: K(0) from all waves; then group B issues its half of
-    // (K(1), V(0)) and takes its offset barrier.
-    dma_tile(kbase, Ks0, 0);
+    // Prologue: K(0) from group A; then group B takes its offset barrier.
+    if (grp == 0) dma_tile(kbase, Ks0, 0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (grp == 1) {
-        if (1 < ntiles) dma_tile(kbase, Ks1, kBN);
-        dma_tile(vbase, Vs0, 0);
-        __syncthreads();
-    }
+    if (grp == 1) __syncthreads();
 
     // Iteration t (t = 0 .. ntiles): phase 1 = PV(t-1) + QK(t), phase 2 =
     // softmax(t).  Buffers: K(t) in Ks[t%2], V(t) in Vs[t%2].
-    auto iteration = [&](int t, const char* Kc, char* Knext, const char* Vprev, char* Vcur, char* Kafter,
-                         char* Vnext) __attribute__((always_inline)) {
+    auto iteration = [&](int t, const char* Kc, char* Knext, const char* Vprev, char* Vcur)
+                         __attribute__((always_inline)) {
         // ---- phase 1
-        if (grp == 0) {
+        mfma_phase(t > 0, Vprev, t < ntiles, Kc);
+        if (grp == 0) {  // the whole tile pair, while group B finishes its softmax
             if (t + 1 < ntiles) dma_tile(kbase, Knext, (t + 1) * kBN);
             if (t < ntiles) dma_tile(vbase, Vcur, t * kBN);
         }
-        mfma_phase(t > 0, Vprev, t < ntiles, Kc);
-        if (grp == 1) __builtin_amdgcn_s_waitcnt(0);  // group B's DMA of (K(t+1), V(t))
         __syncthreads();
         // ---- phase 2
-        if (grp == 1) {
-            if (t + 2 < ntiles) dma_tile(kbase, Kafter, (t + 2) * kBN);
-            if (t + 1 < ntiles) dma_tile(vbase, Vnext, (t + 1) * kBN);
-        }
         if (t < ntiles) softmax_phase(t);
         if (grp == 0) __builtin_amdgcn_s_waitcnt(0);  // group A's DMA of (K(t+1), V(t))
         __syncthreads();
     };
     for (int t = 0; t <= ntiles; t += 2) {
-        // t even: K(t) in Ks0, K(t+1) -> Ks1, V(t-1) in Vs1, V(t) -> Vs0, K(t+2) -> Ks0, V(t+1) -> Vs1
-        iteration(t, Ks0, Ks1, Vs1, Vs0, Ks0, Vs1);
+        // t even: K(t) in Ks0, K(t+1) -> Ks1, V(t-1) in Vs1, V(t) -> Vs0
+        iteration(t, Ks0, Ks1, Vs1, Vs0);
         if (t + 1 > ntiles) break;
-        iteration(t + 1, Ks1, Ks0, Vs0, Vs1, Ks1, Vs0);
+        iteration(t + 1, Ks1, Ks0, Vs0, Vs1);
     }
     if (grp == 0) __syncthreads();  // matches group B's offset barrier
 
