@@ -162,3 +162,18 @@ def test_product_path_has_no_cpu_fallback():
             src = open(os.path.join(pkg, name)).read()
             assert not re.search(r"^\s*(import|from)\s+(\.\.)?oracle\b", src, flags=re.M), name
             assert "import_module" not in src and "__import__" not in src, name
+
+
+def test_asm_load_guard_flags_early_use():
+    """The build-time ISA check: a register of an inline-asm load may be touched
+    only after the vmcnt wait that retires that load."""
+    from attention_causal_gqa_amd.build import _asm_load_hazards
+    head = "k:\n;;#ASMSTART\n\tglobal_load_dwordx4 v[50:53], v[34:35], off\n;;#ASMEND\n"
+    assert _asm_load_hazards(head + "\tv_mov_b32_e32 v34, v50\n\ts_waitcnt vmcnt(0)\n")
+    # loads retire in issue order: vmcnt(1) retires the older plain load, not the asm one
+    young = "k:\n\tglobal_load_dword v9, v[2:3], off\n;;#ASMSTART\n\tglobal_load_dwordx4 v[50:53], v[34:35], off\n;;#ASMEND\n"
+    assert _asm_load_hazards(young + "\ts_waitcnt vmcnt(1)\n\tv_add_f32_e32 v1, v52, v1\n")
+    assert not _asm_load_hazards(young + "\ts_waitcnt vmcnt(0)\n\tv_add_f32_e32 v1, v52, v1\n")
+    assert not _asm_load_hazards(head + "\tglobal_load_dword v9, v[2:3], off\n\ts_waitcnt vmcnt(1)\n"
+                                        "\tv_add_f32_e32 v1, v1, v2\n\ts_waitcnt vmcnt(0)\n\tv_mov_b32_e32 v1, v9\n")
+    assert not _asm_load_hazards(head + "\ts_waitcnt vmcnt(0)\n\tv_mov_b32_e32 v34, v50\n")
