@@ -26,5 +26,6 @@ from .attention import (  # noqa: F401
     gather_pages,
     kv_head_of,
     prefill,
+    prefill_paged,
     prefill_rows,
 )

@@ -26,6 +26,16 @@ design notes of the repository):
   the Softmax / ScaledDotProductAttention primitives of the llm-from-scratch
   "Project Overview" page ("Core Stack: llm/").
 
+  Chunked prefill over a paged cache: the last Tq tokens of each sequence
+  (a chunk of a long prompt processed after its prefix) attend over the
+  sequence's L = seq_lens[b] cached tokens, their own K/V already appended.
+  Query i of the chunk stands at position L - Tq + i and sees keys
+  0..L - Tq + i: the causal mask aligned to the bottom-right corner of the
+  Tq x L score block (RoseLLM README, "Systems highlights", "Inference and
+  serving": chunked prefill and prefix reuse over the paged cache).  Decode
+  is the case Tq = 1; a chunk that is the whole sequence (L = Tq) is the
+  dense prefill above.
+
   Paged decode: one query per sequence, standing at position L-1 of a
   sequence of L = seq_lens[b] cached tokens, so it sees keys 0..L-1 (its own
   K/V already appended).  Token j lives in physical page
@@ -163,4 +173,45 @@ def decode_paged(q, k_pages, v_pages, block_table, seq_lens, scale, page_size):
             vals = gather_pages(v_pages, bt[b], L, page_size, kv)
             o, s = _attend(q[b, h][None, :], keys, vals, float(scale), np.ones((1, L), dtype=bool))
             out[b, h], lse[b, h] = o[0], s[0]
+    return out, lse
+
+
+def prefill_paged(q, k_pages, v_pages, block_table, seq_lens, scale, page_size, rows=None):
+    """Chunked causal prefill over a paged KV cache (bottom-right aligned mask).
+
+    q [B,Hq,Tq,d]; k_pages/v_pages [num_pages,Hkv,page_size,d]; block_table
+    [B, W] int; seq_lens [B] int with Tq <= seq_lens[b] <= W * page_size.
+    Query i of sequence b sees keys 0..seq_lens[b] - Tq + i.  ``rows``, if
+    given, lists the chunk rows to compute (the others are left 0 / -inf).
+    Returns (out [B,Hq,Tq,d], lse [B,Hq,Tq]).
+    """
+    q = _as64(q)
+    if q.ndim != 4:
+        raise ValueError("q must be [B, Hq, Tq, d]")
+    B, Hq, Tq, d = q.shape
+    Hkv = k_pages.shape[1]
+    if k_pages.shape != v_pages.shape or k_pages.shape[2] != page_size or k_pages.shape[3] != d:
+        raise ValueError("page pools must be [num_pages, Hkv, page_size, d]")
+    bt = np.asarray(block_table)
+    sl = np.asarray(seq_lens)
+    if bt.shape[0] != B or sl.shape != (B,):
+        raise ValueError("block_table must be [B, W] and seq_lens [B]")
+    kv_head_of(0, Hq, Hkv)
+    rows = np.arange(Tq) if rows is None else np.asarray(rows, dtype=np.int64)
+    out = np.zeros((B, Hq, Tq, d))
+    lse = np.full((B, Hq, Tq), -np.inf)
+    if Tq == 0 or rows.size == 0:
+        return out, lse
+    for b in range(B):
+        ctx = int(sl[b])
+        if ctx < Tq or ctx > bt.shape[1] * page_size:
+            raise ValueError(f"seq_lens[{b}]={ctx} outside [Tq={Tq}, W*page_size]")
+        pos = ctx - Tq + rows                     # position of each computed query
+        visible = np.arange(ctx)[None, :] <= pos[:, None]
+        for h in range(Hq):
+            kvh = kv_head_of(h, Hq, Hkv)
+            keys = gather_pages(k_pages, bt[b], ctx, page_size, kvh)
+            vals = gather_pages(v_pages, bt[b], ctx, page_size, kvh)
+            o, s = _attend(q[b, h, rows], keys, vals, float(scale), visible)
+            out[b, h, rows], lse[b, h, rows] = o, s
     return out, lse

@@ -276,6 +276,100 @@ def test_p9_decode_brute_force():
             assert abs(lse[b, h] - s) < 1e-13
 
 
+# ---------------------------------------------------------------- chunked prefill over pages
+def chunk_case(seed, Ls, Tq, Hq=4, Hkv=2, d=3, ps=4):
+    """Dense K/V of len max(Ls) per sequence, scattered into one shuffled NaN pool; q for the chunk."""
+    r = rng(seed)
+    B, T = len(Ls), max(Ls)
+    k = r.standard_normal((B, Hkv, T, d))
+    v = r.standard_normal((B, Hkv, T, d))
+    W = -(-T // ps)
+    P = sum(-(-L // ps) for L in Ls)
+    perm = r.permutation(P)
+    table = np.full((B, W), -1)
+    kp = np.full((P, Hkv, ps, d), np.nan)
+    vp = np.full((P, Hkv, ps, d), np.nan)
+    off = 0
+    for b, L in enumerate(Ls):
+        n = -(-L // ps)
+        table[b, :n] = perm[off : off + n]
+        off += n
+        for j in range(L):
+            kp[table[b, j // ps], :, j % ps] = k[b, :, j]
+            vp[table[b, j // ps], :, j % ps] = v[b, :, j]
+    q = 2.0 * r.standard_normal((B, Hq, Tq, d))
+    return q, k, v, kp, vp, table, np.array(Ls), ps
+
+
+def test_chunk_is_the_tail_of_a_dense_prefill():
+    """Rows L-Tq..L-1 of a dense causal prefill over the whole sequence are the chunk's rows."""
+    Ls, Tq = [7, 11, 5], 5
+    q, k, v, kp, vp, table, L, ps = chunk_case(30, Ls, Tq)
+    out, lse = oracle.prefill_paged(q, kp, vp, table, L, 0.7, ps)
+    for b, Lb in enumerate(Ls):
+        qd = np.zeros((1, q.shape[1], Lb, q.shape[3]))
+        qd[0, :, Lb - Tq :] = q[b]
+        od, ld = oracle.prefill(qd, k[b : b + 1, :, :Lb], v[b : b + 1, :, :Lb], 0.7)
+        np.testing.assert_allclose(out[b], od[0, :, Lb - Tq :], rtol=0, atol=1e-13)
+        np.testing.assert_allclose(lse[b], ld[0, :, Lb - Tq :], rtol=0, atol=1e-13)
+
+
+def test_chunk_of_one_token_is_decode():
+    Ls = [1, 6, 9]
+    q, k, v, kp, vp, table, L, ps = chunk_case(31, Ls, 1)
+    out, lse = oracle.prefill_paged(q, kp, vp, table, L, 0.9, ps)
+    od, ld = oracle.decode_paged(q[:, :, 0], kp, vp, table, L, 0.9, ps)
+    np.testing.assert_allclose(out[:, :, 0], od, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(lse[:, :, 0], ld, rtol=0, atol=1e-13)
+
+
+def test_chunk_zero_query_is_prefix_mean():
+    """q = 0: query i of sequence b averages v over keys 0..L_b-Tq+i; lse = ln(L_b-Tq+i+1)."""
+    Ls, Tq = [6, 13], 4
+    q, k, v, kp, vp, table, L, ps = chunk_case(32, Ls, Tq, Hq=4, Hkv=2)
+    v[:, 1] += 5.0  # distinct values per kv head
+    for b, Lb in enumerate(Ls):
+        for j in range(Lb):
+            vp[table[b, j // ps], :, j % ps] = v[b, :, j]
+    out, lse = oracle.prefill_paged(np.zeros_like(q), kp, vp, table, L, 0.5, ps)
+    for b, Lb in enumerate(Ls):
+        for h in range(4):
+            for i in range(Tq):
+                p = Lb - Tq + i
+                np.testing.assert_allclose(out[b, h, i], v[b, h // 2, : p + 1].mean(axis=0), rtol=0, atol=1e-13)
+                assert abs(lse[b, h, i] - math.log(p + 1)) < 1e-13
+
+
+def test_chunk_page_permutation_and_rows():
+    Ls, Tq = [9, 14], 6
+    q, k, v, kp, vp, table, L, ps = chunk_case(33, Ls, Tq)
+    out, lse = oracle.prefill_paged(q, kp, vp, table, L, 0.6, ps)
+    r = rng(34)
+    perm = r.permutation(kp.shape[0])
+    inv = np.argsort(perm)
+    t2 = np.where(table >= 0, perm[np.maximum(table, 0)], -1)
+    out2, lse2 = oracle.prefill_paged(q, kp[inv], vp[inv], t2, L, 0.6, ps)
+    np.testing.assert_array_equal(out2, out)
+    np.testing.assert_array_equal(lse2, lse)
+    rows = [0, 3, 5]
+    out3, lse3 = oracle.prefill_paged(q, kp, vp, table, L, 0.6, ps, rows=rows)
+    np.testing.assert_allclose(out3[:, :, rows], out[:, :, rows], rtol=0, atol=1e-14)
+    np.testing.assert_allclose(lse3[:, :, rows], lse[:, :, rows], rtol=0, atol=1e-14)
+
+
+def test_chunk_brute_force():
+    Ls, Tq = [3, 5], 3
+    q, k, v, kp, vp, table, L, ps = chunk_case(35, Ls, Tq, Hq=2, Hkv=1, d=2, ps=2)
+    out, lse = oracle.prefill_paged(q, kp, vp, table, L, 0.8, ps)
+    for b, Lb in enumerate(Ls):
+        for h in range(2):
+            for i in range(Tq):
+                p = Lb - Tq + i
+                o, s = _mp_attention_row(q[b, h, i], k[b, 0, : p + 1], v[b, 0, : p + 1], 0.8)
+                np.testing.assert_allclose(out[b, h, i], o, rtol=0, atol=1e-14)
+                assert abs(lse[b, h, i] - s) < 1e-13
+
+
 # ---------------------------------------------------------------- golden closed forms
 def _read_fixture(name):
     header, rows, cols = {}, [], None

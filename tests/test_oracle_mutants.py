@@ -51,6 +51,11 @@ MUTATIONS = {
         ("            kv = kv_head_of(h, Hq, Hkv)\n            keys", "            kv = h % Hkv\n            keys"),
     ],
     "empty sequence lse 0": [("lse = np.full((B, Hq), -np.inf)", "lse = np.zeros((B, Hq))")],
+    "chunk mask aligned top-left": [("pos = ctx - Tq + rows", "pos = rows")],
+    "chunk sees one future key": [("pos = ctx - Tq + rows", "pos = ctx - Tq + rows + 1")],
+    "chunk misses its own key": [("np.arange(ctx)[None, :] <= pos[:, None]", "np.arange(ctx)[None, :] < pos[:, None]")],
+    "chunk heads taken modulo": [("kvh = kv_head_of(h, Hq, Hkv)", "kvh = h % Hkv")],
+    "chunk reads the first rows' queries": [("_attend(q[b, h, rows]", "_attend(q[b, h, : rows.size]")],
 }
 
 
