@@ -50,6 +50,11 @@ def load_library():
     lib.attn_decode_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, i32, i32,
                                       vp, sz, vp]
     lib.attn_decode_paged.restype = i32
+    lib.attn_prefill_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, f32, i32,
+                                       vp]
+    lib.attn_prefill_paged.restype = i32
+    lib.attn_validate_chunk_metadata.argtypes = [vp, vp, i32, i32, i32, i32, i32]
+    lib.attn_validate_chunk_metadata.restype = i32
     lib.attn_validate_paged_metadata.argtypes = [vp, vp, i32, i32, i32, i32]
     lib.attn_validate_paged_metadata.restype = i32
     lib.attn_status_string.argtypes = [i32]
@@ -135,6 +140,40 @@ def attn_prefill(q, k, v, out=None, lse=None, scale=None, stream=None):
     return out, (None if lse is False else lse)
 
 
+def attn_prefill_paged(q, k_pages, v_pages, block_table, seq_lens, out=None, lse=None, scale=None, stream=None):
+    """Chunked causal prefill over a paged cache.  q [B,Hq,Tq,d] (the last Tq tokens of each sequence);
+    pools [P,Hkv,page,d]; block_table [B,W] int32; seq_lens [B] int32 (>= Tq) -> (out, lse fp32 [B,Hq,Tq])."""
+    torch = _torch()
+    _require(q.dim() == 4 and k_pages.dim() == 4 and k_pages.shape == v_pages.shape, "bad q / page pool shapes")
+    B, Hq, Tq, d = q.shape
+    P, Hkv, page_size, dk = k_pages.shape
+    _require(dk == d, "page pools and q disagree on d")
+    _require(block_table.dim() == 2 and block_table.shape[0] == B and block_table.dtype == torch.int32,
+             "block_table must be int32 [B, W]")
+    _require(seq_lens.shape == (B,) and seq_lens.dtype == torch.int32, "seq_lens must be int32 [B]")
+    for n, t in (("q", q), ("k_pages", k_pages), ("v_pages", v_pages), ("block_table", block_table),
+                 ("seq_lens", seq_lens)):
+        _dense_on_gpu(n, t)
+    _require(q.dtype == k_pages.dtype == v_pages.dtype, "q and the page pools must share a dtype")
+    W = block_table.shape[1]
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hq, Tq), dtype=torch.float32, device=q.device)
+    _dense_on_gpu("out", out)
+    _require(out.shape == q.shape and out.dtype == q.dtype, "out must match q")
+    if lse is not False:
+        _dense_on_gpu("lse", lse)
+        _require(lse.shape == (B, Hq, Tq) and lse.dtype == torch.float32, "lse must be float32 [B, Hq, Tq]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    _check(load_library().attn_prefill_paged(_ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table),
+                                             _ptr(seq_lens), _ptr(out), None if lse is False else _ptr(lse), B, Hq,
+                                             Hkv, Tq, d, page_size, P, W, float(scale), _dtype_code(q),
+                                             _stream(stream)))
+    return out, (None if lse is False else lse)
+
+
 def attn_decode_num_splits(B, Hq, Hkv, d, page_size, max_pages_per_seq, num_splits=0):
     s = load_library().attn_decode_num_splits(B, Hq, Hkv, d, page_size, max_pages_per_seq, num_splits)
     _check(min(s, 0))
@@ -193,3 +232,15 @@ def attn_validate_paged_metadata(block_table, seq_lens, page_size, num_pages):
     sl = np.ascontiguousarray(np.asarray(seq_lens.cpu() if hasattr(seq_lens, "cpu") else seq_lens, dtype=np.int32))
     B, W = bt.shape
     _check(load_library().attn_validate_paged_metadata(bt.ctypes.data, sl.ctypes.data, B, W, page_size, num_pages))
+
+
+def attn_validate_chunk_metadata(block_table, seq_lens, page_size, num_pages, chunk_len):
+    """attn_validate_paged_metadata plus seq_lens >= chunk_len (host copies); raises AttnError if out of contract."""
+    import numpy as np
+
+    bt = np.ascontiguousarray(np.asarray(block_table.cpu() if hasattr(block_table, "cpu") else block_table,
+                                         dtype=np.int32))
+    sl = np.ascontiguousarray(np.asarray(seq_lens.cpu() if hasattr(seq_lens, "cpu") else seq_lens, dtype=np.int32))
+    B, W = bt.shape
+    _check(load_library().attn_validate_chunk_metadata(bt.ctypes.data, sl.ctypes.data, B, W, page_size, num_pages,
+                                                       chunk_len))

@@ -40,6 +40,7 @@ constexpr int kPageSize = 16;
 constexpr int kMaxDecodeGroup = 16;
 constexpr int kMaxPrefillGroup = 128;
 constexpr int64_t kMaxGrid = 0x7fffffff;
+constexpr int kMaxChunkTablePages = 8192;  // block-table entries the chunked prefill stages in LDS
 
 // ---- decode split plan ------------------------------------------------------
 struct Plan {
@@ -140,6 +141,48 @@ int attn_prefill(const void* q, const void* k, const void* v, void* out, float* 
     return from_hip(e, "attn_prefill launch");
 }
 
+int attn_prefill_paged(const void* q, const void* k_pages, const void* v_pages, const int32_t* block_table,
+                       const int32_t* seq_lens, void* out, float* lse, int B, int Hq, int Hkv, int Tq, int d,
+                       int page_size, int num_pages, int max_pages_per_seq, float scale, attn_dtype_t dtype,
+                       hipStream_t stream) {
+    g_last_error.clear();
+    if (dtype != ATTN_F32 && dtype != ATTN_BF16) return fail(ATTN_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
+    if (B < 0 || Tq < 0) return fail(ATTN_ERR_INVALID_ARG, "B=%d, Tq=%d must be >= 0", B, Tq);
+    if (Hq < 1 || Hkv < 1) return fail(ATTN_ERR_INVALID_ARG, "Hq=%d, Hkv=%d must be >= 1", Hq, Hkv);
+    if (Hq % Hkv != 0) return fail(ATTN_ERR_INVALID_ARG, "Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
+    if (d < 1) return fail(ATTN_ERR_INVALID_ARG, "d=%d must be >= 1", d);
+    if (page_size < 1) return fail(ATTN_ERR_INVALID_ARG, "page_size=%d must be >= 1", page_size);
+    if (max_pages_per_seq < 1) return fail(ATTN_ERR_INVALID_ARG, "max_pages_per_seq=%d must be >= 1", max_pages_per_seq);
+    if (num_pages < 0) return fail(ATTN_ERR_INVALID_ARG, "num_pages=%d must be >= 0", num_pages);
+    if ((int64_t)max_pages_per_seq * page_size > 0x7fffffff)
+        return fail(ATTN_ERR_INVALID_ARG, "max_pages_per_seq * page_size overflows int");
+    if ((int64_t)Tq > (int64_t)max_pages_per_seq * page_size)
+        return fail(ATTN_ERR_INVALID_ARG, "Tq=%d exceeds the cache capacity max_pages_per_seq * page_size", Tq);
+    if (!std::isfinite(scale)) return fail(ATTN_ERR_INVALID_ARG, "scale must be finite");
+    if (dtype != ATTN_BF16) return fail(ATTN_ERR_UNSUPPORTED, "chunked prefill supports ATTN_BF16 only");
+    if (d != 64 && d != 128) return fail(ATTN_ERR_UNSUPPORTED, "chunked prefill supports d = 64 or 128, not %d", d);
+    if (page_size != kPageSize)
+        return fail(ATTN_ERR_UNSUPPORTED, "chunked prefill supports page_size = 16, not %d", page_size);
+    if (Hq / Hkv > kMaxPrefillGroup)
+        return fail(ATTN_ERR_UNSUPPORTED, "chunked prefill supports Hq/Hkv <= %d", kMaxPrefillGroup);
+    if (max_pages_per_seq > kMaxChunkTablePages)
+        return fail(ATTN_ERR_UNSUPPORTED, "chunked prefill supports max_pages_per_seq <= %d", kMaxChunkTablePages);
+    if (B == 0 || Tq == 0) return ATTN_OK;
+    if (!q || !k_pages || !v_pages || !block_table || !seq_lens || !out)
+        return fail(ATTN_ERR_INVALID_ARG, "q, k_pages, v_pages, block_table, seq_lens and out must be non-null");
+    if (!aligned(q, 16) || !aligned(k_pages, 16) || !aligned(v_pages, 16) || !aligned(out, 16))
+        return fail(ATTN_ERR_INVALID_ARG, "q, k_pages, v_pages and out must be 16-byte aligned");
+    if (!aligned(block_table, 4) || !aligned(seq_lens, 4) || (lse && !aligned(lse, 4)))
+        return fail(ATTN_ERR_INVALID_ARG, "block_table, seq_lens and lse must be 4-byte aligned");
+    const int64_t rows_per_block = 256 / (Hq / Hkv);
+    const int64_t blocks = (Tq + rows_per_block - 1) / rows_per_block * B * Hkv;
+    if (blocks > kMaxGrid) return fail(ATTN_ERR_INVALID_ARG, "problem too large: %lld workgroups", (long long)blocks);
+
+    attn::PrefillArgs a{q, k_pages, v_pages, out, lse, B, Hq, Hkv, Tq, d, scale};
+    return from_hip(attn::launch_prefill_paged_bf16(a, block_table, seq_lens, max_pages_per_seq, stream),
+                    "attn_prefill_paged launch");
+}
+
 int attn_decode_num_splits(int B, int Hq, int Hkv, int d, int page_size, int max_pages_per_seq, int num_splits) {
     g_last_error.clear();
     int st = check_decode_sizes(B, Hq, Hkv, d, page_size, max_pages_per_seq, num_splits);
@@ -187,6 +230,20 @@ int attn_decode_paged(const void* q, const void* k_pages, const void* v_pages, c
                        Hq,     Hkv,      d,       page_size,   max_pages_per_seq, plan.splits,
                        plan.pages_per_split, scale};
     return from_hip(attn::launch_decode_bf16(a, stream), "attn_decode_paged launch");
+}
+
+int attn_validate_chunk_metadata(const int32_t* block_table_host, const int32_t* seq_lens_host, int B,
+                                 int max_pages_per_seq, int page_size, int num_pages, int chunk_len) {
+    g_last_error.clear();
+    if (chunk_len < 0) return fail(ATTN_ERR_INVALID_ARG, "chunk_len=%d must be >= 0", chunk_len);
+    const int st = attn_validate_paged_metadata(block_table_host, seq_lens_host, B, max_pages_per_seq, page_size,
+                                                num_pages);
+    if (st != ATTN_OK) return st;
+    for (int b = 0; b < B; ++b)
+        if (seq_lens_host[b] < chunk_len)
+            return fail(ATTN_ERR_INVALID_ARG, "seq_lens[%d]=%d is shorter than the chunk (%d)", b, seq_lens_host[b],
+                        chunk_len);
+    return ATTN_OK;
 }
 
 int attn_validate_paged_metadata(const int32_t* block_table_host, const int32_t* seq_lens_host, int B,

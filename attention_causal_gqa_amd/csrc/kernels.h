@@ -35,6 +35,10 @@ struct DecodeArgs {
 
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream);
+// Chunked prefill over a paged cache: a.k / a.v are the page pools
+// [num_pages, Hkv, 16, d], a.T is the chunk length; block_table [B, W].
+hipError_t launch_prefill_paged_bf16(const PrefillArgs& a, const int32_t* block_table, const int32_t* seq_lens, int W,
+                                     hipStream_t stream);
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream);
 
 }  // namespace attn

@@ -50,6 +50,8 @@ namespace {
 
 constexpr int kRows = 256;  // query rows (token, head pairs) per workgroup
 constexpr int kBN = 64;     // keys per tile
+constexpr int kPage = 16;   // tokens per page of a paged cache
+constexpr int kMaxTablePages = 8192;  // block-table entries staged in LDS (contexts up to 131072 tokens)
 
 // XOR swizzle of 16-byte chunks within an LDS row of CPR chunks: chunk c of
 // row r is stored at position c ^ swz(r).  With CPR = 16 (256-byte rows),
@@ -107,11 +109,21 @@ __device__ __forceinline__ void dma16(const void* g, char* lds_base) {
 // drains while A would otherwise wait at the barrier), into the buffers last
 // read in slots 2t-2 and 2t-1; A waits for it before the barrier that ends
 // slot 2t+1.
-template <int D, bool kPosScale>
+//
+// kPaged: chunked prefill over a paged cache.  k and v are then page pools
+// [num_pages, Hkv, 16, D]; the T queries of sequence b are its last T
+// tokens, so query t stands at position pos0 + t with pos0 = seq_lens[b] - T
+// and sees keys 0 .. pos0 + t (the causal mask aligned to the bottom-right
+// corner).  The block-table entries the workgroup needs are staged in LDS
+// once; each DMA row then finds its page there.  With pos0 = 0 and dense
+// K/V this is the plain prefill.
+template <int D, bool kPosScale, bool kPaged>
 __global__ __launch_bounds__(512, 1) void prefill_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                                                               const bf16* __restrict__ v, bf16* __restrict__ out,
                                                               float* __restrict__ lse, int B, int Hq, int Hkv, int T,
-                                                              int G, int BMt, int nqb, float c1) {
+                                                              int G, int BMt, int nqb, float c1,
+                                                              const int* __restrict__ block_table,
+                                                              const int* __restrict__ seq_lens, int W) {
     constexpr int CPR = D / 8;            // 16-byte chunks per key row
     constexpr int ROWB = D * 2;           // bytes per key row (no padding: rows are swizzled)
     constexpr int TILEB = kBN * ROWB;     // bytes per K or V tile
@@ -131,7 +143,8 @@ __global__ __launch_bounds__(512, 1) void prefill_bf16_kernel(const bf16* __rest
     // (the lse pointer is otherwise first used after the key loop) makes the
     // compiler wait for all LDS reads at every LDS wait inside the loop,
     // because scalar loads can complete out of order.
-    __asm__ volatile("" ::"s"(q), "s"(k), "s"(v), "s"(out), "s"(lse));
+    __asm__ volatile("" ::"s"(q), "s"(k), "s"(v), "s"(out), "s"(lse), "s"(block_table), "s"(seq_lens));
+    __shared__ int bt_lds[kPaged ? kMaxTablePages : 1];  // the sequence's block table (paged form)
 
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index 0..7, in an SGPR
@@ -146,6 +159,13 @@ __global__ __launch_bounds__(512, 1) void prefill_bf16_kernel(const bf16* __rest
     const int b = pair / Hkv;
     const int kvh = pair % Hkv;
     const int t0 = qb * BMt;
+    // Keys of the sequence (Lkv) and the position of query 0 (pos0).
+    int Lkv = T, pos0 = 0;
+    if constexpr (kPaged) {
+        Lkv = seq_lens[b];
+        pos0 = Lkv - T;
+    }
+    const int kend = pos0 + min(t0 + BMt, T);  // keys 0..kend-1 are visible to some row
 
     // This lane's query column: row r of the workgroup (256 rows).
     const int r = 32 * w + l32;
@@ -167,8 +187,8 @@ __global__ __launch_bounds__(512, 1) void prefill_bf16_kernel(const bf16* __rest
     // i.e. rows RPI*n .. RPI*n + RPI-1; lane l lands at row RPI*n + l / CPR,
     // swizzled position l % CPR, so it fetches logical chunk (l % CPR) ^ swz(row).
     // Wave w owns DMAs w*NIW .. w*NIW + NIW-1 of every tile.
-    const bf16* kbase = k + (size_t)(b * Hkv + kvh) * T * D;
-    const bf16* vbase = v + (size_t)(b * Hkv + kvh) * T * D;
+    const bf16* kbase = kPaged ? k + (size_t)kvh * kPage * D : k + (size_t)(b * Hkv + kvh) * T * D;
+    const bf16* vbase = kPaged ? v + (size_t)kvh * kPage * D : v + (size_t)(b * Hkv + kvh) * T * D;
     // Group A (waves 0-3) issues every DMA: wave w takes the DMAs of wave
     // slots w and w + 4, i.e. DMAs w*NIW .. and (w+4)*NIW .. of every tile.
     constexpr int NDW = 2 * NIW;
@@ -181,10 +201,23 @@ __global__ __launch_bounds__(512, 1) void prefill_bf16_kernel(const bf16* __rest
         drow[j] = RPI * dslot[j] + lane / CPR;
         doff[j] = (uint32_t)(drow[j] * ROWB + 16 * ((lane % CPR) ^ swz<CPR>(drow[j])));
     }
-    // Keys past T are read as key T-1: they are masked for every stored row
-    // (key >= T > token), and V is finite, so they add exact zeros.
+    // Keys at or past kend (the paged form) or T (the dense form) are read
+    // as the last one before it: they are masked for every row of the
+    // workgroup (their positions are below kend), and V is finite, so they
+    // add exact zeros.  The paged form must not go past kend - 1: only the
+    // block-table entries of keys 0..kend-1 are staged.
     auto dma_tile = [&](const bf16* base, char* dst, int k0) __attribute__((always_inline)) {
-        if (k0 + kBN <= T) {
+        if constexpr (kPaged) {
+            // (page, kv head) slices are kPage rows of ROWB bytes, Hkv slices per page.
+            const char* bb = reinterpret_cast<const char*>(base);
+#pragma unroll
+            for (int j = 0; j < NDW; ++j) {
+                const int key = min(k0 + drow[j], kend - 1);
+                const size_t page = (size_t)bt_lds[key / kPage];
+                dma16(bb + (page * Hkv * kPage + key % kPage) * ROWB + (doff[j] - (uint32_t)(drow[j] * ROWB)),
+                      dst + 1024 * dslot[j]);
+            }
+        } else if (k0 + kBN <= T) {
             const char* tb = reinterpret_cast<const char*>(base + (size_t)k0 * D);
 #pragma unroll
             for (int j = 0; j < NDW; ++j) dma16(tb + doff[j], dst + 1024 * dslot[j]);
@@ -239,9 +272,8 @@ __global__ __launch_bounds__(512, 1) void prefill_bf16_kernel(const bf16* __rest
     float l_lse = 0.f;        // the same sum over fp32 p (for the log-sum-exp)
 
     const float cc = kPosScale ? c1 : 1.f;
-    const int kend = min(t0 + BMt, T);
     const int ntiles = (kend + kBN - 1) / kBN;
-    const int first_diag = (t0 + 1) / kBN;   // tiles from here on reach past token t0
+    const int first_diag = (pos0 + t0 + 1) / kBN;  // tiles from here on reach past row t0's position
     constexpr uint32_t kOnes = 0x3F803F80u;  // two bf16 1.0
 
     // MFMA phase: O^T += V^T(t-1) P^T(t-1), then S^T(t) = K(t) Q^T.
@@ -310,14 +342,15 @@ __global__ __launch_bounds__(512, 1) void prefill_bf16_kernel(const bf16* __rest
 #pragma unroll
                 for (int i = 0; i < 16; ++i) sacc[kb][i] *= c1;
         }
-        // Causal mask on tiles that reach past the workgroup's first token.
-        // Element i of block kb is key k0 + 32kb + 8(i/4) + 4hi + i%4: masked
-        // when 32kb + 8(i/4) + i%4 > token - k0 - 4hi.
+        // Causal mask on tiles that reach past the position of the
+        // workgroup's first row.  Element i of block kb is key k0 + 32kb +
+        // 8(i/4) + 4hi + i%4: masked when 32kb + 8(i/4) + i%4 > pos0 + token
+        // - k0 - 4hi.
         if (t >= first_diag) {
             // A real (wave-uniform) branch: the empty volatile asm keeps the
             // compiler from turning the mask into selects run on every tile.
             __asm__ volatile("" ::: "memory");
-            const int thr = token - k0 - 4 * hi;
+            const int thr = pos0 + token - k0 - 4 * hi;
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -391,7 +424,14 @@ __global__ __launch_bounds__(512, 1) void prefill_bf16_kernel(const bf16* __rest
         l_lse += (lsum[0] + lsum[1]) + (lsum[2] + lsum[3]);
     };
 
-    // Prologue: K(0) from group A; then group B takes its offset barrier.
+    // Prologue: the block table (paged form), K(0) from group A; then group
+    // B takes its offset barrier.
+    if constexpr (kPaged) {
+        const int need = (kend + kPage - 1) / kPage;
+        const int* row = block_table + (size_t)b * W;
+        for (int i = tid; i < need; i += 512) bt_lds[i] = row[i];
+        __syncthreads();
+    }
     if (grp == 0) dma_tile(kbase, Ks0, 0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -440,21 +480,21 @@ __global__ __launch_bounds__(512, 1) void prefill_bf16_kernel(const bf16* __rest
     }
 }
 
-template <int D>
-hipError_t launch_d(const PrefillArgs& a, hipStream_t stream) {
+template <int D, bool kPaged>
+hipError_t launch_d(const PrefillArgs& a, const int* block_table, const int* seq_lens, int W, hipStream_t stream) {
     const int G = a.Hq / a.Hkv;
     const int BMt = kRows / G;
     const int nqb = (a.T + BMt - 1) / BMt;
     const dim3 grid((unsigned)nqb * a.B * a.Hkv);
     const float c1 = (float)((double)a.scale * 1.4426950408889634);
     if (c1 > 0.f) {
-        hipLaunchKernelGGL((prefill_bf16_kernel<D, true>), grid, dim3(512), 0, stream, (const bf16*)a.q,
+        hipLaunchKernelGGL((prefill_bf16_kernel<D, true, kPaged>), grid, dim3(512), 0, stream, (const bf16*)a.q,
                            (const bf16*)a.k, (const bf16*)a.v, (bf16*)a.out, a.lse, a.B, a.Hq, a.Hkv, a.T, G, BMt,
-                           nqb, c1);
+                           nqb, c1, block_table, seq_lens, W);
     } else {
-        hipLaunchKernelGGL((prefill_bf16_kernel<D, false>), grid, dim3(512), 0, stream, (const bf16*)a.q,
+        hipLaunchKernelGGL((prefill_bf16_kernel<D, false, kPaged>), grid, dim3(512), 0, stream, (const bf16*)a.q,
                            (const bf16*)a.k, (const bf16*)a.v, (bf16*)a.out, a.lse, a.B, a.Hq, a.Hkv, a.T, G, BMt,
-                           nqb, c1);
+                           nqb, c1, block_table, seq_lens, W);
     }
     return hipGetLastError();
 }
@@ -462,7 +502,14 @@ hipError_t launch_d(const PrefillArgs& a, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream) {
-    return a.d == 128 ? launch_d<128>(a, stream) : launch_d<64>(a, stream);
+    return a.d == 128 ? launch_d<128, false>(a, nullptr, nullptr, 0, stream)
+                      : launch_d<64, false>(a, nullptr, nullptr, 0, stream);
+}
+
+hipError_t launch_prefill_paged_bf16(const PrefillArgs& a, const int32_t* block_table, const int32_t* seq_lens, int W,
+                                     hipStream_t stream) {
+    return a.d == 128 ? launch_d<128, true>(a, block_table, seq_lens, W, stream)
+                      : launch_d<64, true>(a, block_table, seq_lens, W, stream);
 }
 
 }  // namespace attn

@@ -49,6 +49,34 @@ class DecodeShape:
         return -(-self.L_hi // self.page_size)
 
 
+@dataclass(frozen=True)
+class ChunkShape:
+    """Chunked prefill over a paged cache: the last Tq tokens of sequences of L ~ U{L_lo..L_hi} cached tokens."""
+    B: int
+    Hq: int
+    Hkv: int
+    Tq: int
+    d: int
+    page_size: int
+    L_lo: int
+    L_hi: int
+    dtype: torch.dtype
+
+    @property
+    def max_pages_per_seq(self) -> int:
+        return -(-self.L_hi // self.page_size)
+
+
+def chunk_flops(Hq, d, Tq, seq_lens) -> int:
+    """Algorithmic flops of a chunked prefill: QK^T and PV over each query's visible keys.
+
+    Query t of a sequence of L tokens sees L - Tq + t + 1 keys, so a sequence contributes
+    Tq (L - Tq) + Tq (Tq + 1) / 2 query-key pairs, at 2 flops per multiply-add and two products.
+    """
+    pairs = sum(Tq * (int(L) - Tq) + Tq * (Tq + 1) // 2 for L in seq_lens)
+    return 4 * Hq * d * pairs
+
+
 # The five workloads.  Prefill inputs are drawn with seed = workload number,
 # decode inputs with seed = 100 + workload number.
 WORKLOADS = {
@@ -62,12 +90,16 @@ WORKLOADS = {
     },
 }
 
+# Chunked prefill (seed 6): 2048-token chunks at the end of sequences of 4096..16384 cached tokens.
+WORKLOADS[6] = {"chunk": ChunkShape(4, 32, 8, 2048, 128, PAGE_SIZE, 4096, 16384, torch.bfloat16)}
+
 WORKLOAD_NAMES = {
     1: "causal MHA prefill fp32 B1 H4 T128 d64",
     2: "causal GQA prefill bf16 B1 Hq16 Hkv8 T512 d128",
     3: "causal GQA prefill bf16 B2 Hq32 Hkv8 T2048 d128",
     4: "paged decode bf16 B32 Hq16 Hkv8 d128 page16 L~U[32,2048]",
     5: "mixed: prefill bf16 B1 Hq32 Hkv8 T8192 d128 + paged decode bf16 B64 Hq32 Hkv8 d128 page16 L~U[1024,8192]",
+    6: "chunked prefill bf16 over a paged cache B4 Hq32 Hkv8 Tq2048 d128 page16 L~U[4096,16384]",
 }
 
 
@@ -155,6 +187,38 @@ def paged_inputs(shape: DecodeShape, seed: int, *, seq_lens=None, extra_pages=0,
         _poison(k_pages, table, seq_lens, shape.page_size, extra_pages, poison)
         _poison(v_pages, table, seq_lens, shape.page_size, extra_pages, poison)
     return PagedInputs(q, k_pages, v_pages, table, seq_lens.to(torch.int32), shape.page_size)
+
+
+@dataclass
+class ChunkInputs:
+    q: torch.Tensor            # [B, Hq, Tq, d]
+    k_pages: torch.Tensor      # [num_pages, Hkv, page_size, d]
+    v_pages: torch.Tensor      # [num_pages, Hkv, page_size, d]
+    block_table: torch.Tensor  # [B, W] int32, unused entries -1
+    seq_lens: torch.Tensor     # [B] int32, each >= Tq
+    page_size: int
+
+
+def chunk_inputs(shape: ChunkShape, seed: int, *, seq_lens=None, poison=None, B=None):
+    """Chunked-prefill inputs: seq_lens ~ U{L_lo..L_hi} (unless given), pool in randperm order, q for the chunk.
+
+    Draw order: seq_lens, page permutation, q, K pool, V pool.  ``poison`` fills every unused slot.
+    """
+    g = torch.Generator().manual_seed(seed)
+    B = shape.B if B is None else B
+    if seq_lens is None:
+        seq_lens = torch.randint(shape.L_lo, shape.L_hi + 1, (B,), generator=g)
+    seq_lens = torch.as_tensor(seq_lens, dtype=torch.int64)
+    W = shape.max_pages_per_seq
+    table, num_pages = _pool_layout(seq_lens, shape.page_size, W, g, 0)
+    q = torch.randn(B, shape.Hq, shape.Tq, shape.d, generator=g).to(shape.dtype)
+    pool_shape = (num_pages, shape.Hkv, shape.page_size, shape.d)
+    k_pages = torch.randn(pool_shape, generator=g).to(shape.dtype)
+    v_pages = torch.randn(pool_shape, generator=g).to(shape.dtype)
+    if poison is not None:
+        _poison(k_pages, table, seq_lens, shape.page_size, 0, poison)
+        _poison(v_pages, table, seq_lens, shape.page_size, 0, poison)
+    return ChunkInputs(q, k_pages, v_pages, table, seq_lens.to(torch.int32), shape.page_size)
 
 
 def paged_from_dense(k, v, seq_lens, page_size, seed, W=None, poison=None):

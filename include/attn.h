@@ -19,6 +19,13 @@
  *    It runs as a split-KV kernel writing partial results, followed by a
  *    log-sum-exp combine kernel.
  *
+ *  - attn_prefill_paged: chunked prefill over the paged cache: the last Tq
+ *    tokens of each sequence (a chunk processed after the sequence's prefix
+ *    was cached, as in the chunked prefill and prefix reuse of the RoseLLM
+ *    README, "Systems highlights", "Inference and serving") attend over all
+ *    of the sequence's cached keys, causally.  It is the prefill kernel
+ *    reading its key/value tiles page by page through the block table.
+ *
  * What is computed.  For query head h, the kv head read is h / (Hq / Hkv)
  * (consecutive groups of query heads share one kv head).  For a query q and
  * its visible keys k_j with values v_j:
@@ -27,6 +34,9 @@
  * Prefill: query t sees keys 0..t (inclusive).  Decode: the query of
  * sequence b stands at position seq_lens[b]-1 and sees keys
  * 0..seq_lens[b]-1, so its own key and value must already be in the cache.
+ * Chunked prefill: query t of sequence b stands at position
+ * seq_lens[b] - Tq + t and sees keys 0..seq_lens[b] - Tq + t (the chunk's
+ * own keys and values must already be in the cache).
  *
  * Conventions for every entry point.
  *  - Pointers marked "device" are device memory owned by the caller; the
@@ -83,6 +93,35 @@ typedef enum attn_dtype {
 int attn_prefill(const void* q, const void* k, const void* v, void* out, float* lse,
                  int B, int Hq, int Hkv, int T, int d, float scale,
                  attn_dtype_t dtype, hipStream_t stream);
+
+/*
+ * Chunked causal prefill over a paged KV cache (see the file header).
+ *
+ *   q, out         : device, [B, Hq, Tq, d] in `dtype`; row t of sequence b
+ *                    is the query at position seq_lens[b] - Tq + t
+ *   k_pages,v_pages: device, [num_pages, Hkv, page_size, d] in `dtype`, as
+ *                    for attn_decode_paged
+ *   block_table    : device int32 [B, max_pages_per_seq], as for decode;
+ *                    entries past ceil(seq_lens[b] / page_size) are never read
+ *   seq_lens       : device int32 [B]; cached tokens per sequence, the chunk
+ *                    included: each in [Tq, max_pages_per_seq * page_size]
+ *   lse            : device float32 [B, Hq, Tq], or NULL to skip it
+ *   B, Tq          : >= 0 (either 0 enqueues nothing and returns ATTN_OK)
+ *   Hq, Hkv        : >= 1, Hq % Hkv == 0, Hq / Hkv <= 128
+ *   dtype          : ATTN_BF16; d = 128 or 64; page_size = 16;
+ *                    max_pages_per_seq <= 8192 (contexts up to 131072 tokens)
+ * out is written with round-to-nearest-even from the fp32 accumulator; q and
+ * the cached tokens must hold finite values, other slots may hold anything.
+ * The block table and seq_lens are read on the device only; values outside
+ * the ranges above are undefined behaviour (check them with
+ * attn_validate_chunk_metadata).  No workspace is needed.
+ */
+int attn_prefill_paged(const void* q, const void* k_pages, const void* v_pages,
+                       const int32_t* block_table, const int32_t* seq_lens,
+                       void* out, float* lse,
+                       int B, int Hq, int Hkv, int Tq, int d, int page_size, int num_pages,
+                       int max_pages_per_seq, float scale, attn_dtype_t dtype,
+                       hipStream_t stream);
 
 /*
  * Split plan of attn_decode_paged: the number of splits S each sequence's
@@ -144,6 +183,14 @@ int attn_decode_paged(const void* q, const void* k_pages, const void* v_pages,
  */
 int attn_validate_paged_metadata(const int32_t* block_table_host, const int32_t* seq_lens_host,
                                  int B, int max_pages_per_seq, int page_size, int num_pages);
+
+/*
+ * attn_validate_paged_metadata plus the chunked-prefill condition
+ * seq_lens[b] >= chunk_len for every sequence.  Host only; touches no device.
+ */
+int attn_validate_chunk_metadata(const int32_t* block_table_host, const int32_t* seq_lens_host,
+                                 int B, int max_pages_per_seq, int page_size, int num_pages,
+                                 int chunk_len);
 
 /* Static description of a status code (never NULL). */
 const char* attn_status_string(int status);

@@ -27,8 +27,9 @@ def declared_functions():
 
 def test_header_declares_the_api():
     names = declared_functions()
-    for n in ("attn_prefill", "attn_decode_paged", "attn_decode_workspace_bytes", "attn_decode_num_splits",
-              "attn_validate_paged_metadata", "attn_status_string", "attn_last_error_message"):
+    for n in ("attn_prefill", "attn_prefill_paged", "attn_decode_paged", "attn_decode_workspace_bytes",
+              "attn_decode_num_splits", "attn_validate_paged_metadata", "attn_validate_chunk_metadata",
+              "attn_status_string", "attn_last_error_message"):
         assert n in names
 
 
@@ -118,6 +119,55 @@ def test_decode_rejects(lib, kw, status):
 
 def test_decode_empty_batch_is_a_no_op(lib):
     assert decode(lib, q=None, kp=None, vp=None, bt=None, sl=None, out=None, B=0, ws=None, wsb=0) == A.ATTN_OK
+
+
+def prefill_paged(lib, q=FAKE, kp=FAKE, vp=FAKE, bt=FAKE, sl=FAKE, out=FAKE, lse=None, B=2, Hq=4, Hkv=2, Tq=40,
+                  d=128, ps=16, P=10, W=8, scale=0.1, dtype=1):
+    return lib.attn_prefill_paged(q, kp, vp, bt, sl, out, lse, B, Hq, Hkv, Tq, d, ps, P, W, scale, dtype, None)
+
+
+@pytest.mark.parametrize(
+    "kw,status",
+    [
+        (dict(q=None), A.ATTN_ERR_INVALID_ARG),
+        (dict(bt=None), A.ATTN_ERR_INVALID_ARG),
+        (dict(sl=None), A.ATTN_ERR_INVALID_ARG),
+        (dict(out=None), A.ATTN_ERR_INVALID_ARG),
+        (dict(kp=FAKE + 4), A.ATTN_ERR_INVALID_ARG),
+        (dict(bt=FAKE + 2), A.ATTN_ERR_INVALID_ARG),
+        (dict(lse=FAKE + 1), A.ATTN_ERR_INVALID_ARG),
+        (dict(Hq=5, Hkv=2), A.ATTN_ERR_INVALID_ARG),
+        (dict(B=-1), A.ATTN_ERR_INVALID_ARG),
+        (dict(Tq=-1), A.ATTN_ERR_INVALID_ARG),
+        (dict(Tq=8 * 16 + 1), A.ATTN_ERR_INVALID_ARG),  # longer than the cache can hold
+        (dict(W=0), A.ATTN_ERR_INVALID_ARG),
+        (dict(P=-1), A.ATTN_ERR_INVALID_ARG),
+        (dict(scale=float("inf")), A.ATTN_ERR_INVALID_ARG),
+        (dict(dtype=5), A.ATTN_ERR_INVALID_ARG),
+        (dict(dtype=0), A.ATTN_ERR_UNSUPPORTED),
+        (dict(d=96), A.ATTN_ERR_UNSUPPORTED),
+        (dict(ps=32, Tq=40), A.ATTN_ERR_UNSUPPORTED),
+        (dict(Hq=256, Hkv=1), A.ATTN_ERR_UNSUPPORTED),
+        (dict(W=8193), A.ATTN_ERR_UNSUPPORTED),
+    ],
+)
+def test_prefill_paged_rejects(lib, kw, status):
+    assert prefill_paged(lib, **kw) == status
+    assert A.attn_last_error_message() != ""
+
+
+def test_prefill_paged_empty_is_a_no_op(lib):
+    assert prefill_paged(lib, q=None, kp=None, vp=None, bt=None, sl=None, out=None, B=0) == A.ATTN_OK
+    assert prefill_paged(lib, q=None, kp=None, vp=None, bt=None, sl=None, out=None, Tq=0) == A.ATTN_OK
+
+
+def test_validate_chunk_metadata():
+    bt = np.array([[3, 1, -1], [0, 2, -1]], dtype=np.int32)
+    A.attn_validate_chunk_metadata(bt, np.array([20, 32], dtype=np.int32), 16, 4, 20)
+    with pytest.raises(A.AttnError):
+        A.attn_validate_chunk_metadata(bt, np.array([19, 32], dtype=np.int32), 16, 4, 20)  # shorter than the chunk
+    with pytest.raises(A.AttnError):
+        A.attn_validate_chunk_metadata(bt, np.array([33, 32], dtype=np.int32), 16, 4, 20)  # reads entry -1
 
 
 def test_split_plan_and_workspace(lib):
