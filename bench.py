@@ -15,7 +15,10 @@ each part, in a second pass of K steps whose launches are queued while the
 GPU runs a short sleep kernel, so that the events time kernels rather than
 host launch latency.
 
-    python bench.py [--steps K] [--warmup W] [--workload 5|3|4] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--workload 5|3|4|6] [--no-cpu-baseline]
+
+Workload 6 (not the default) times the chunked prefill over a paged cache:
+2048-token chunks at the end of four sequences of 4096..16384 cached tokens.
     python bench.py --copy-calibration   # plain 1 GiB copy, reference for HBM byte counters
 """
 
@@ -47,7 +50,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workload", type=int, default=5, choices=(3, 4, 5))
+    p.add_argument("--workload", type=int, default=5, choices=(3, 4, 5, 6))
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--flush", action="store_true",
                    help="write a 512 MiB buffer before each step (outside the kernel events) to evict L2/MALL")
@@ -148,6 +151,33 @@ def cpu_baseline(pre_inputs, pre_shape, dec_inputs, budget_s=20.0):
     }
 
 
+def cpu_baseline_chunk(inp, budget_s=20.0):
+    """Time the fp64 oracle on a bounded sample of the chunked-prefill workload: sequence 0, head by head."""
+    import oracle
+    from threadpoolctl import threadpool_info
+
+    threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    B, Hq, Tq, d = inp.q.shape
+    Hkv = inp.k_pages.shape[1]
+    g = Hq // Hkv
+    kp, vp = inp.k_pages.float().numpy(), inp.v_pages.float().numpy()
+    L = int(inp.seq_lens[0])
+    scale = synth.fp32_scale(d)
+    t0 = time.perf_counter()
+    heads = 0
+    while heads < Hq and (heads == 0 or time.perf_counter() - t0 < budget_s):
+        h = heads
+        oracle.prefill_paged(inp.q[0:1, h:h + 1].float().numpy(), kp[:, h // g:h // g + 1], vp[:, h // g:h // g + 1],
+                             inp.block_table[0:1].numpy(), inp.seq_lens[0:1].numpy(), scale, inp.page_size)
+        heads += 1
+    t = time.perf_counter() - t0
+    flops = heads * synth.chunk_flops(1, d, Tq, [L])
+    return {"value": flops / t / PEAK_BF16_FLOPS, "unit": "fraction of MI355X roofline", "cores": threads,
+            "kind": "oracle",
+            "sample": f"fp64 oracle: chunked prefill of sequence 0 (L={L}), {heads} of {Hq} query heads ({t:.2f} s)",
+            "chunk_tflops": flops / t / 1e12, "host_cpu_count": os.cpu_count()}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -162,8 +192,9 @@ def main():
     wl = synth.WORKLOADS[args.workload]
     pre_shape = wl.get("prefill")
     dec_shape = wl.get("decode")
+    chunk_shape = wl.get("chunk")
 
-    pre_inputs = dec_inputs = None
+    pre_inputs = dec_inputs = chunk_in = None
     work = {}
     if pre_shape is not None:
         pre_inputs = synth.prefill_inputs(pre_shape, seed=args.workload)
@@ -185,6 +216,14 @@ def main():
         dscale = synth.fp32_scale(dec_shape.d)
         work["decode"] = lambda: A.attn_decode_paged(dq, kp, vp, bt, sl, out=dout, lse=dlse, scale=dscale,
                                                      workspace=ws)
+    if chunk_shape is not None:
+        chunk_in = synth.chunk_inputs(chunk_shape, seed=args.workload)
+        cq, ckp, cvp, cbt, csl = (t.to(dev) for t in (chunk_in.q, chunk_in.k_pages, chunk_in.v_pages,
+                                                      chunk_in.block_table, chunk_in.seq_lens))
+        cout = torch.empty_like(cq)
+        clse = torch.empty(cq.shape[:3], dtype=torch.float32, device=dev)
+        cscale = synth.fp32_scale(chunk_shape.d)
+        work["chunk"] = lambda: A.attn_prefill_paged(cq, ckp, cvp, cbt, csl, out=cout, lse=clse, scale=cscale)
     flush_buf = torch.empty(512 << 20, dtype=torch.uint8, device=dev) if args.flush else None
 
     names = list(work)
@@ -249,15 +288,22 @@ def main():
                            "num_splits": A.attn_decode_num_splits(dec_shape.B, dec_shape.Hq, dec_shape.Hkv,
                                                                   dec_shape.d, dec_shape.page_size,
                                                                   dec_inputs.max_pages_per_seq, 0)}
+    if chunk_shape is not None:
+        flops = synth.chunk_flops(chunk_shape.Hq, chunk_shape.d, chunk_shape.Tq, chunk_in.seq_lens.tolist())
+        t = ms["chunk"] / 1e3
+        at_peak += flops / PEAK_BF16_FLOPS
+        parts["chunk"] = {"ms": round(ms["chunk"], 4), "ms_min": round(min(per["chunk"]), 4),
+                          "tflops": round(flops / t / 1e12, 1), "frac_of_peak": round(flops / t / PEAK_BF16_FLOPS, 4),
+                          "flops_per_launch": flops}
     value = at_peak / (ms_per_step / 1e3)
 
     # Dominant kernel's roofline (the one with the larger share of the step).
     dom = max(names, key=lambda n: ms[n])
-    if dom == "prefill":
+    if dom in ("prefill", "chunk"):
         src = kernel_source_hash(["prefill_bf16.hip", "device_common.h"])
-        roof = {"kernel": "prefill_bf16_kernel", "bound": "mfma", "achieved": parts["prefill"]["tflops"],
-                "peak": PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s",
-                "frac": round(parts["prefill"]["tflops"] * 1e12 / PEAK_BF16_FLOPS, 4),
+        roof = {"kernel": "prefill_bf16_kernel" + (" (paged form)" if dom == "chunk" else ""), "bound": "mfma",
+                "achieved": parts[dom]["tflops"], "peak": PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s",
+                "frac": round(parts[dom]["tflops"] * 1e12 / PEAK_BF16_FLOPS, 4),
                 "traffic": measured_traffic(args.workload, "prefill_bf16_kernel", src), "source_hash": src}
     else:
         src = kernel_source_hash(["decode_paged.hip", "device_common.h"])
@@ -267,10 +313,15 @@ def main():
                 "traffic": measured_traffic(args.workload, "decode_stream_kernel+decode_combine_kernel", src),
                 "source_hash": src}
 
-    cfg = {"workload": synth.WORKLOAD_NAMES[args.workload], "seed_prefill": args.workload,
-           "seed_decode": 100 + args.workload}
+    cfg = {"workload": synth.WORKLOAD_NAMES[args.workload]}
+    if pre_shape is not None:
+        cfg["seed_prefill"] = args.workload
     if dec_inputs is not None:
+        cfg["seed_decode"] = 100 + args.workload
         cfg["decode_tokens"] = int(dec_inputs.seq_lens.sum())
+    if chunk_in is not None:
+        cfg["seed_chunk"] = args.workload
+        cfg["chunk_seq_lens"] = chunk_in.seq_lens.tolist()
     result.update({
         "value": round(value, 4),
         "unit": "fraction of MI355X roofline (step time at peak / measured step time)",
@@ -285,6 +336,8 @@ def main():
     })
     if not args.no_cpu_baseline and args.workload == 5:
         result["cpu_baseline"] = cpu_baseline(pre_inputs, pre_shape, dec_inputs)
+    if not args.no_cpu_baseline and args.workload == 6:
+        result["cpu_baseline"] = cpu_baseline_chunk(chunk_in)
     print(json.dumps(result), flush=True)
 
 
