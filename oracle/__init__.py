@@ -24,6 +24,7 @@ source and checks that the pins catch each one.
 from .attention import (  # noqa: F401
     decode_paged,
     gather_pages,
+    kv_append,
     kv_head_of,
     prefill,
     prefill_paged,

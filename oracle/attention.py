@@ -215,3 +215,36 @@ def prefill_paged(q, k_pages, v_pages, block_table, seq_lens, scale, page_size, 
             o, s = _attend(q[b, h, rows], keys, vals, float(scale), visible)
             out[b, h, rows], lse[b, h, rows] = o, s
     return out, lse
+
+
+def kv_append(k_pages, v_pages, k_new, v_new, block_table, seq_lens, page_size):
+    """Write the newest tokens' keys and values into their paged-cache slots.
+
+    The cache write that precedes attention over a paged cache (the KV-cache
+    writer of the RoseLLM README, "Systems highlights", "Inference and
+    serving").  k_new/v_new [B, Hkv, Tn, d] are the last Tn tokens of each
+    sequence, whose length after the append is seq_lens[b] (>= Tn): token t
+    goes to position seq_lens[b] - Tn + t, i.e. slot position % page_size of
+    page block_table[b][position // page_size], for every kv head.  Returns
+    new pools (copies); every other slot keeps its value.  Values are copied
+    unchanged (no arithmetic).
+    """
+    k_out = np.array(k_pages, copy=True)
+    v_out = np.array(v_pages, copy=True)
+    B, Hkv, Tn, d = np.shape(k_new)
+    bt = np.asarray(block_table)
+    sl = np.asarray(seq_lens)
+    if np.shape(v_new) != (B, Hkv, Tn, d) or k_out.shape[1:] != (Hkv, page_size, d):
+        raise ValueError("k_new/v_new must be [B, Hkv, Tn, d] and the pools [P, Hkv, page_size, d]")
+    for b in range(B):
+        total = int(sl[b])
+        if total < Tn or total > bt.shape[1] * page_size:
+            raise ValueError(f"seq_lens[{b}]={total} outside [Tn={Tn}, W*page_size]")
+        for t in range(Tn):
+            position = total - Tn + t
+            page = int(bt[b, position // page_size])
+            if page < 0 or page >= k_out.shape[0]:
+                raise ValueError("block table names a page outside the pool")
+            k_out[page, :, position % page_size] = np.asarray(k_new)[b, :, t]
+            v_out[page, :, position % page_size] = np.asarray(v_new)[b, :, t]
+    return k_out, v_out

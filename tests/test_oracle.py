@@ -370,6 +370,50 @@ def test_chunk_brute_force():
                 assert abs(lse[b, h, i] - s) < 1e-13
 
 
+# ---------------------------------------------------------------- KV append into the paged cache
+def test_append_then_gather_returns_the_new_tokens():
+    """Positions L-Tn..L-1 read back through the table are k_new / v_new; every other slot is untouched."""
+    r = rng(40)
+    ps, Hkv, d, Tn = 4, 3, 5, 6
+    Ls = [6, 9, 17]
+    W = 5
+    P = sum(-(-L // ps) for L in Ls) + 2
+    perm = r.permutation(P)
+    table = np.full((3, W), -1)
+    off = 0
+    for b, L in enumerate(Ls):
+        n = -(-L // ps)
+        table[b, :n] = perm[off : off + n]
+        off += n
+    kp, vp = r.standard_normal((P, Hkv, ps, d)), r.standard_normal((P, Hkv, ps, d))
+    kn, vn = r.standard_normal((3, Hkv, Tn, d)), r.standard_normal((3, Hkv, Tn, d))
+    k2, v2 = oracle.kv_append(kp, vp, kn, vn, table, np.array(Ls), ps)
+    written = np.zeros((P, ps), dtype=bool)
+    for b, L in enumerate(Ls):
+        for kvh in range(Hkv):
+            np.testing.assert_array_equal(oracle.gather_pages(k2, table[b], L, ps, kvh)[L - Tn :], kn[b, kvh])
+            np.testing.assert_array_equal(oracle.gather_pages(v2, table[b], L, ps, kvh)[L - Tn :], vn[b, kvh])
+        for j in range(L - Tn, L):
+            written[table[b, j // ps], j % ps] = True
+    slots = lambda x: x.transpose(0, 2, 1, 3)  # [page, slot, kv head, d]
+    np.testing.assert_array_equal(slots(k2)[~written], slots(kp)[~written])
+    np.testing.assert_array_equal(slots(v2)[~written], slots(vp)[~written])
+
+
+def test_append_then_decode_equals_dense_history():
+    """Cache the first L-1 tokens densely, append the last one, decode: same as the prefill's last row."""
+    q, k, v = gqa_case(41, B=1, Hq=4, Hkv=2, T=11, d=4)
+    L, ps = 11, 4
+    kp, vp, table = paged_copy(k[0], v[0], L - 1, ps, seed=42, extra_pages=1)
+    if -(-L // ps) > -(-(L - 1) // ps):  # the new token opens a page: give it the spare one
+        table[(L - 1) // ps] = kp.shape[0] - 1
+    k2, v2 = oracle.kv_append(kp, vp, k[:, :, L - 1 : L], v[:, :, L - 1 : L], table[None], np.array([L]), ps)
+    od, ld = oracle.decode_paged(q[:, :, L - 1], k2, v2, table[None], np.array([L]), 0.6, ps)
+    op, lp = oracle.prefill(q, k, v, 0.6)
+    np.testing.assert_allclose(od, op[:, :, L - 1], rtol=0, atol=1e-13)
+    np.testing.assert_allclose(ld, lp[:, :, L - 1], rtol=0, atol=1e-13)
+
+
 # ---------------------------------------------------------------- golden closed forms
 def _read_fixture(name):
     header, rows, cols = {}, [], None

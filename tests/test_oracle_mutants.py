@@ -56,6 +56,14 @@ MUTATIONS = {
     "chunk misses its own key": [("np.arange(ctx)[None, :] <= pos[:, None]", "np.arange(ctx)[None, :] < pos[:, None]")],
     "chunk heads taken modulo": [("kvh = kv_head_of(h, Hq, Hkv)", "kvh = h % Hkv")],
     "chunk reads the first rows' queries": [("_attend(q[b, h, rows]", "_attend(q[b, h, : rows.size]")],
+    "append one position late": [("position = total - Tn + t", "position = total - Tn + t + 1")],
+    "append at the sequence start": [("position = total - Tn + t", "position = t")],
+    "append page and slot swapped": [
+        ("page = int(bt[b, position // page_size])", "page = int(bt[b, position % page_size])"),
+        ("k_out[page, :, position % page_size]", "k_out[page, :, position // page_size]"),
+    ],
+    "append writes V into K": [("k_out[page, :, position % page_size] = np.asarray(k_new)[b, :, t]",
+                                "k_out[page, :, position % page_size] = np.asarray(v_new)[b, :, t]")],
 }
 
 
