@@ -53,6 +53,8 @@ def load_library():
     lib.attn_prefill_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, f32, i32,
                                        vp]
     lib.attn_prefill_paged.restype = i32
+    lib.attn_kv_append.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, vp]
+    lib.attn_kv_append.restype = i32
     lib.attn_validate_chunk_metadata.argtypes = [vp, vp, i32, i32, i32, i32, i32]
     lib.attn_validate_chunk_metadata.restype = i32
     lib.attn_validate_paged_metadata.argtypes = [vp, vp, i32, i32, i32, i32]
@@ -172,6 +174,28 @@ def attn_prefill_paged(q, k_pages, v_pages, block_table, seq_lens, out=None, lse
                                              Hkv, Tq, d, page_size, P, W, float(scale), _dtype_code(q),
                                              _stream(stream)))
     return out, (None if lse is False else lse)
+
+
+def attn_kv_append(k_new, v_new, k_pages, v_pages, block_table, seq_lens, stream=None):
+    """Write the last Tn tokens of each sequence into the paged cache, in place.  k_new/v_new [B,Hkv,Tn,d];
+    pools [P,Hkv,page,d]; block_table [B,W] int32; seq_lens [B] int32 = lengths after the append (>= Tn)."""
+    torch = _torch()
+    _require(k_new.dim() == 4 and k_new.shape == v_new.shape, "k_new and v_new must be [B, Hkv, Tn, d]")
+    _require(k_pages.dim() == 4 and k_pages.shape == v_pages.shape, "bad page pool shapes")
+    B, Hkv, Tn, d = k_new.shape
+    P, Hkv_p, page_size, dk = k_pages.shape
+    _require(Hkv_p == Hkv and dk == d, "page pools and k_new disagree on Hkv or d")
+    _require(block_table.dim() == 2 and block_table.shape[0] == B and block_table.dtype == torch.int32,
+             "block_table must be int32 [B, W]")
+    _require(seq_lens.shape == (B,) and seq_lens.dtype == torch.int32, "seq_lens must be int32 [B]")
+    for n, t in (("k_new", k_new), ("v_new", v_new), ("k_pages", k_pages), ("v_pages", v_pages),
+                 ("block_table", block_table), ("seq_lens", seq_lens)):
+        _dense_on_gpu(n, t)
+    _require(k_new.dtype == v_new.dtype == k_pages.dtype == v_pages.dtype, "k_new, v_new and the pools must share a dtype")
+    _check(load_library().attn_kv_append(_ptr(k_new), _ptr(v_new), _ptr(k_pages), _ptr(v_pages), _ptr(block_table),
+                                         _ptr(seq_lens), B, Hkv, Tn, d, page_size, P, block_table.shape[1],
+                                         _dtype_code(k_new), _stream(stream)))
+    return k_pages, v_pages
 
 
 def attn_decode_num_splits(B, Hq, Hkv, d, page_size, max_pages_per_seq, num_splits=0):

@@ -19,7 +19,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libattn.so")
 ARCH = "gfx950"
 
-SOURCES = ["attn_api.cpp", "prefill_f32.hip", "prefill_bf16.hip", "decode_paged.hip"]
+SOURCES = ["attn_api.cpp", "prefill_f32.hip", "prefill_bf16.hip", "decode_paged.hip", "kv_append.hip"]
 
 # Per-source extra flags.  The bf16 prefill's softmax sees only finite scores
 # and -inf (never NaN: inputs are finite by contract), so NaN-quieting

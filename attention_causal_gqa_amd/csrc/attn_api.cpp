@@ -183,6 +183,34 @@ int attn_prefill_paged(const void* q, const void* k_pages, const void* v_pages, 
                     "attn_prefill_paged launch");
 }
 
+int attn_kv_append(const void* k_new, const void* v_new, void* k_pages, void* v_pages, const int32_t* block_table,
+                   const int32_t* seq_lens, int B, int Hkv, int Tn, int d, int page_size, int num_pages,
+                   int max_pages_per_seq, attn_dtype_t dtype, hipStream_t stream) {
+    g_last_error.clear();
+    if (dtype != ATTN_F32 && dtype != ATTN_BF16) return fail(ATTN_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
+    if (B < 0 || Tn < 0) return fail(ATTN_ERR_INVALID_ARG, "B=%d, Tn=%d must be >= 0", B, Tn);
+    if (Hkv < 1) return fail(ATTN_ERR_INVALID_ARG, "Hkv=%d must be >= 1", Hkv);
+    if (d < 1) return fail(ATTN_ERR_INVALID_ARG, "d=%d must be >= 1", d);
+    if (page_size < 1) return fail(ATTN_ERR_INVALID_ARG, "page_size=%d must be >= 1", page_size);
+    if (max_pages_per_seq < 1) return fail(ATTN_ERR_INVALID_ARG, "max_pages_per_seq=%d must be >= 1", max_pages_per_seq);
+    if (num_pages < 0) return fail(ATTN_ERR_INVALID_ARG, "num_pages=%d must be >= 0", num_pages);
+    if ((int64_t)Tn > (int64_t)max_pages_per_seq * page_size)
+        return fail(ATTN_ERR_INVALID_ARG, "Tn=%d exceeds the cache capacity max_pages_per_seq * page_size", Tn);
+    if ((int64_t)B * Hkv * Tn > 0x7fffffff) return fail(ATTN_ERR_INVALID_ARG, "B * Hkv * Tn overflows int");
+    if (dtype != ATTN_BF16) return fail(ATTN_ERR_UNSUPPORTED, "KV append supports ATTN_BF16 only");
+    if (d != 64 && d != 128) return fail(ATTN_ERR_UNSUPPORTED, "KV append supports d = 64 or 128, not %d", d);
+    if (page_size != kPageSize) return fail(ATTN_ERR_UNSUPPORTED, "KV append supports page_size = 16, not %d", page_size);
+    if (B == 0 || Tn == 0) return ATTN_OK;
+    if (!k_new || !v_new || !k_pages || !v_pages || !block_table || !seq_lens)
+        return fail(ATTN_ERR_INVALID_ARG, "k_new, v_new, k_pages, v_pages, block_table and seq_lens must be non-null");
+    if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(k_pages, 16) || !aligned(v_pages, 16))
+        return fail(ATTN_ERR_INVALID_ARG, "k_new, v_new, k_pages and v_pages must be 16-byte aligned");
+    if (!aligned(block_table, 4) || !aligned(seq_lens, 4))
+        return fail(ATTN_ERR_INVALID_ARG, "block_table and seq_lens must be 4-byte aligned");
+    attn::KvAppendArgs a{k_new, v_new, k_pages, v_pages, block_table, seq_lens, B, Hkv, Tn, d, max_pages_per_seq};
+    return from_hip(attn::launch_kv_append_bf16(a, stream), "attn_kv_append launch");
+}
+
 int attn_decode_num_splits(int B, int Hq, int Hkv, int d, int page_size, int max_pages_per_seq, int num_splits) {
     g_last_error.clear();
     int st = check_decode_sizes(B, Hq, Hkv, d, page_size, max_pages_per_seq, num_splits);

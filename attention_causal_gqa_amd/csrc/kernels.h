@@ -33,6 +33,16 @@ struct DecodeArgs {
     float scale;
 };
 
+struct KvAppendArgs {
+    const void* k_new;           // [B, Hkv, Tn, d]
+    const void* v_new;           // [B, Hkv, Tn, d]
+    void* k_pages;               // [num_pages, Hkv, 16, d]
+    void* v_pages;               // [num_pages, Hkv, 16, d]
+    const int32_t* block_table;  // [B, W]
+    const int32_t* seq_lens;     // [B], lengths after the append
+    int B, Hkv, Tn, d, W;
+};
+
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream);
 // Chunked prefill over a paged cache: a.k / a.v are the page pools
@@ -40,5 +50,6 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_prefill_paged_bf16(const PrefillArgs& a, const int32_t* block_table, const int32_t* seq_lens, int W,
                                      hipStream_t stream);
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_kv_append_bf16(const KvAppendArgs& a, hipStream_t stream);
 
 }  // namespace attn

@@ -93,6 +93,9 @@ WORKLOADS = {
 # Chunked prefill (seed 6): 2048-token chunks at the end of sequences of 4096..16384 cached tokens.
 WORKLOADS[6] = {"chunk": ChunkShape(4, 32, 8, 2048, 128, PAGE_SIZE, 4096, 16384, torch.bfloat16)}
 
+# KV append (seed 7): the 2048-token chunks of workload 6's shape written into the paged cache.
+WORKLOADS[7] = {"append": ChunkShape(4, 32, 8, 2048, 128, PAGE_SIZE, 4096, 16384, torch.bfloat16)}
+
 WORKLOAD_NAMES = {
     1: "causal MHA prefill fp32 B1 H4 T128 d64",
     2: "causal GQA prefill bf16 B1 Hq16 Hkv8 T512 d128",
@@ -100,6 +103,7 @@ WORKLOAD_NAMES = {
     4: "paged decode bf16 B32 Hq16 Hkv8 d128 page16 L~U[32,2048]",
     5: "mixed: prefill bf16 B1 Hq32 Hkv8 T8192 d128 + paged decode bf16 B64 Hq32 Hkv8 d128 page16 L~U[1024,8192]",
     6: "chunked prefill bf16 over a paged cache B4 Hq32 Hkv8 Tq2048 d128 page16 L~U[4096,16384]",
+    7: "KV append bf16 into a paged cache B4 Hkv8 Tn2048 d128 page16 L~U[4096,16384]",
 }
 
 
@@ -219,6 +223,43 @@ def chunk_inputs(shape: ChunkShape, seed: int, *, seq_lens=None, poison=None, B=
         _poison(k_pages, table, seq_lens, shape.page_size, 0, poison)
         _poison(v_pages, table, seq_lens, shape.page_size, 0, poison)
     return ChunkInputs(q, k_pages, v_pages, table, seq_lens.to(torch.int32), shape.page_size)
+
+
+@dataclass
+class AppendInputs:
+    k_new: torch.Tensor        # [B, Hkv, Tn, d]
+    v_new: torch.Tensor        # [B, Hkv, Tn, d]
+    k_pages: torch.Tensor      # [num_pages, Hkv, page_size, d]
+    v_pages: torch.Tensor      # [num_pages, Hkv, page_size, d]
+    block_table: torch.Tensor  # [B, W] int32, unused entries -1
+    seq_lens: torch.Tensor     # [B] int32, lengths after the append (>= Tn)
+    page_size: int
+
+    def algorithmic_bytes(self) -> int:
+        """k_new and v_new read once and written once, plus the block-table entries and seq_lens read."""
+        B, Hkv, Tn, d = self.k_new.shape
+        return 4 * self.k_new.numel() * self.k_new.element_size() + 4 * B * (-(-Tn // self.page_size) + 1)
+
+
+def append_inputs(shape: ChunkShape, seed: int, *, seq_lens=None, poison=None):
+    """KV-append inputs: seq_lens ~ U{L_lo..L_hi} (lengths after the append), pool in randperm order,
+    k_new / v_new [B, Hkv, Tq, d] for the last Tq tokens.  Draw order: seq_lens, page permutation,
+    K pool, V pool, k_new, v_new.  ``poison`` fills every unused slot of the pools."""
+    g = torch.Generator().manual_seed(seed)
+    B = shape.B
+    if seq_lens is None:
+        seq_lens = torch.randint(shape.L_lo, shape.L_hi + 1, (B,), generator=g)
+    seq_lens = torch.as_tensor(seq_lens, dtype=torch.int64)
+    table, num_pages = _pool_layout(seq_lens, shape.page_size, shape.max_pages_per_seq, g, 0)
+    pool_shape = (num_pages, shape.Hkv, shape.page_size, shape.d)
+    k_pages = torch.randn(pool_shape, generator=g).to(shape.dtype)
+    v_pages = torch.randn(pool_shape, generator=g).to(shape.dtype)
+    if poison is not None:
+        _poison(k_pages, table, seq_lens, shape.page_size, 0, poison)
+        _poison(v_pages, table, seq_lens, shape.page_size, 0, poison)
+    k_new = torch.randn(B, shape.Hkv, shape.Tq, shape.d, generator=g).to(shape.dtype)
+    v_new = torch.randn(B, shape.Hkv, shape.Tq, shape.d, generator=g).to(shape.dtype)
+    return AppendInputs(k_new, v_new, k_pages, v_pages, table, seq_lens.to(torch.int32), shape.page_size)
 
 
 def paged_from_dense(k, v, seq_lens, page_size, seed, W=None, poison=None):

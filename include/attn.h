@@ -26,6 +26,11 @@
  *    of the sequence's cached keys, causally.  It is the prefill kernel
  *    reading its key/value tiles page by page through the block table.
  *
+ *  - attn_kv_append: writes the newest tokens' keys and values into their
+ *    slots of the paged cache (the KV-cache writer of the RoseLLM README,
+ *    "Systems highlights", "Inference and serving"), the step before decode
+ *    or chunked prefill reads them.
+ *
  * What is computed.  For query head h, the kv head read is h / (Hq / Hkv)
  * (consecutive groups of query heads share one kv head).  For a query q and
  * its visible keys k_j with values v_j:
@@ -122,6 +127,28 @@ int attn_prefill_paged(const void* q, const void* k_pages, const void* v_pages,
                        int B, int Hq, int Hkv, int Tq, int d, int page_size, int num_pages,
                        int max_pages_per_seq, float scale, attn_dtype_t dtype,
                        hipStream_t stream);
+
+/*
+ * KV append: copy the last Tn tokens' keys and values of each sequence into
+ * the paged cache.
+ *
+ *   k_new, v_new   : device, [B, Hkv, Tn, d] in `dtype`; token t of sequence
+ *                    b goes to position seq_lens[b] - Tn + t
+ *   k_pages,v_pages: device, [num_pages, Hkv, page_size, d] in `dtype`; only
+ *                    the B * Tn written (page, slot) rows change, every kv head
+ *   block_table    : device int32 [B, max_pages_per_seq], as for decode
+ *   seq_lens       : device int32 [B]; each sequence's length after the
+ *                    append, in [Tn, max_pages_per_seq * page_size] (the same
+ *                    array then serves attn_decode_paged or attn_prefill_paged)
+ *   dtype          : ATTN_BF16; d = 128 or 64; page_size = 16
+ * Values are copied bit for bit.  Two appended tokens must not name the same
+ * (page, slot); the block table and seq_lens are read on the device only
+ * (check them with attn_validate_chunk_metadata, chunk_len = Tn).
+ */
+int attn_kv_append(const void* k_new, const void* v_new, void* k_pages, void* v_pages,
+                   const int32_t* block_table, const int32_t* seq_lens,
+                   int B, int Hkv, int Tn, int d, int page_size, int num_pages,
+                   int max_pages_per_seq, attn_dtype_t dtype, hipStream_t stream);
 
 /*
  * Split plan of attn_decode_paged: the number of splits S each sequence's

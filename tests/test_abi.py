@@ -27,7 +27,7 @@ def declared_functions():
 
 def test_header_declares_the_api():
     names = declared_functions()
-    for n in ("attn_prefill", "attn_prefill_paged", "attn_decode_paged", "attn_decode_workspace_bytes",
+    for n in ("attn_prefill", "attn_prefill_paged", "attn_kv_append", "attn_decode_paged", "attn_decode_workspace_bytes",
               "attn_decode_num_splits", "attn_validate_paged_metadata", "attn_validate_chunk_metadata",
               "attn_status_string", "attn_last_error_message"):
         assert n in names
@@ -159,6 +159,40 @@ def test_prefill_paged_rejects(lib, kw, status):
 def test_prefill_paged_empty_is_a_no_op(lib):
     assert prefill_paged(lib, q=None, kp=None, vp=None, bt=None, sl=None, out=None, B=0) == A.ATTN_OK
     assert prefill_paged(lib, q=None, kp=None, vp=None, bt=None, sl=None, out=None, Tq=0) == A.ATTN_OK
+
+
+def kv_append(lib, kn=FAKE, vn=FAKE, kp=FAKE, vp=FAKE, bt=FAKE, sl=FAKE, B=2, Hkv=2, Tn=40, d=128, ps=16, P=10, W=8,
+              dtype=1):
+    return lib.attn_kv_append(kn, vn, kp, vp, bt, sl, B, Hkv, Tn, d, ps, P, W, dtype, None)
+
+
+@pytest.mark.parametrize(
+    "kw,status",
+    [
+        (dict(kn=None), A.ATTN_ERR_INVALID_ARG),
+        (dict(vp=None), A.ATTN_ERR_INVALID_ARG),
+        (dict(bt=None), A.ATTN_ERR_INVALID_ARG),
+        (dict(kn=FAKE + 8), A.ATTN_ERR_INVALID_ARG),
+        (dict(sl=FAKE + 1), A.ATTN_ERR_INVALID_ARG),
+        (dict(B=-1), A.ATTN_ERR_INVALID_ARG),
+        (dict(Tn=-1), A.ATTN_ERR_INVALID_ARG),
+        (dict(Tn=8 * 16 + 1), A.ATTN_ERR_INVALID_ARG),
+        (dict(Hkv=0), A.ATTN_ERR_INVALID_ARG),
+        (dict(W=0), A.ATTN_ERR_INVALID_ARG),
+        (dict(dtype=9), A.ATTN_ERR_INVALID_ARG),
+        (dict(dtype=0), A.ATTN_ERR_UNSUPPORTED),
+        (dict(d=32), A.ATTN_ERR_UNSUPPORTED),
+        (dict(ps=8, Tn=4), A.ATTN_ERR_UNSUPPORTED),
+    ],
+)
+def test_kv_append_rejects(lib, kw, status):
+    assert kv_append(lib, **kw) == status
+    assert A.attn_last_error_message() != ""
+
+
+def test_kv_append_empty_is_a_no_op(lib):
+    assert kv_append(lib, kn=None, vn=None, kp=None, vp=None, bt=None, sl=None, B=0) == A.ATTN_OK
+    assert kv_append(lib, kn=None, vn=None, kp=None, vp=None, bt=None, sl=None, Tn=0) == A.ATTN_OK
 
 
 def test_validate_chunk_metadata():
