@@ -13,12 +13,14 @@ peak plus decode bytes at the HBM peak) divided by the measured step time.
 Per-kernel rates come from HIP events recorded on the launch stream around
 each part, in a second pass of K steps whose launches are queued while the
 GPU runs a short sleep kernel, so that the events time kernels rather than
-host launch latency.
+host launch latency.  A workload with a single part times its K queued
+launches between one pair of events instead (``ms_min`` stays per launch).
 
-    python bench.py [--steps K] [--warmup W] [--workload 5|3|4|6] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--workload 5|3|4|6|7] [--no-cpu-baseline]
 
 Workload 6 (not the default) times the chunked prefill over a paged cache:
 2048-token chunks at the end of four sequences of 4096..16384 cached tokens.
+Workload 7 times the KV append that writes such chunks into the cache.
     python bench.py --copy-calibration   # plain 1 GiB copy, reference for HBM byte counters
 """
 
@@ -50,7 +52,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workload", type=int, default=5, choices=(3, 4, 5, 6))
+    p.add_argument("--workload", type=int, default=5, choices=(3, 4, 5, 6, 7))
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--flush", action="store_true",
                    help="write a 512 MiB buffer before each step (outside the kernel events) to evict L2/MALL")
@@ -178,6 +180,21 @@ def cpu_baseline_chunk(inp, budget_s=20.0):
             "chunk_tflops": flops / t / 1e12, "host_cpu_count": os.cpu_count()}
 
 
+def cpu_baseline_append(inp):
+    """Time the oracle's KV append on the whole workload (bf16 values moved as 16-bit patterns)."""
+    import oracle
+
+    bits = lambda t: t.contiguous().view(torch.int16).numpy()
+    kp, vp, kn, vn = bits(inp.k_pages), bits(inp.v_pages), bits(inp.k_new), bits(inp.v_new)
+    t0 = time.perf_counter()
+    oracle.kv_append(kp, vp, kn, vn, inp.block_table.numpy(), inp.seq_lens.numpy(), inp.page_size)
+    t = time.perf_counter() - t0
+    nbytes = inp.algorithmic_bytes()
+    return {"value": nbytes / t / PEAK_HBM_BYTES, "unit": "fraction of MI355X roofline", "cores": 1, "kind": "oracle",
+            "sample": f"oracle KV append of the whole workload ({t:.2f} s, including its copies of both pools)",
+            "append_gbps": nbytes / t / 1e9, "host_cpu_count": os.cpu_count()}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -193,8 +210,9 @@ def main():
     pre_shape = wl.get("prefill")
     dec_shape = wl.get("decode")
     chunk_shape = wl.get("chunk")
+    app_shape = wl.get("append")
 
-    pre_inputs = dec_inputs = chunk_in = None
+    pre_inputs = dec_inputs = chunk_in = app_in = None
     work = {}
     if pre_shape is not None:
         pre_inputs = synth.prefill_inputs(pre_shape, seed=args.workload)
@@ -224,6 +242,11 @@ def main():
         clse = torch.empty(cq.shape[:3], dtype=torch.float32, device=dev)
         cscale = synth.fp32_scale(chunk_shape.d)
         work["chunk"] = lambda: A.attn_prefill_paged(cq, ckp, cvp, cbt, csl, out=cout, lse=clse, scale=cscale)
+    if app_shape is not None:
+        app_in = synth.append_inputs(app_shape, seed=args.workload)
+        akn, avn, akp, avp, abt, asl = (t.to(dev) for t in (app_in.k_new, app_in.v_new, app_in.k_pages,
+                                                            app_in.v_pages, app_in.block_table, app_in.seq_lens))
+        work["append"] = lambda: A.attn_kv_append(akn, avn, akp, avp, abt, asl)
     flush_buf = torch.empty(512 << 20, dtype=torch.uint8, device=dev) if args.flush else None
 
     names = list(work)
@@ -265,6 +288,19 @@ def main():
 
     per = {n: [evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(args.steps)] for i, n in enumerate(names)}
     ms = {n: float(np.mean(per[n])) for n in names}
+    if len(names) == 1:
+        # One part per step: time the K queued launches between one pair of
+        # events, so that a short kernel's time does not carry the cost of an
+        # event pair per launch (a few microseconds).
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        torch.cuda._sleep(200_000 * args.steps)
+        e0.record(stream)
+        for _ in range(args.steps):
+            step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms[names[0]] = e0.elapsed_time(e1) / args.steps
     kernel_ms = sum(ms.values())
     ms_per_step = wall * 1e3 / args.steps
 
@@ -295,6 +331,13 @@ def main():
         parts["chunk"] = {"ms": round(ms["chunk"], 4), "ms_min": round(min(per["chunk"]), 4),
                           "tflops": round(flops / t / 1e12, 1), "frac_of_peak": round(flops / t / PEAK_BF16_FLOPS, 4),
                           "flops_per_launch": flops}
+    if app_shape is not None:
+        nbytes = app_in.algorithmic_bytes()
+        t = ms["append"] / 1e3
+        at_peak += nbytes / PEAK_HBM_BYTES
+        parts["append"] = {"ms": round(ms["append"], 4), "ms_min": round(min(per["append"]), 4),
+                           "gbps": round(nbytes / t / 1e9, 1), "frac_of_peak": round(nbytes / t / PEAK_HBM_BYTES, 4),
+                           "bytes_per_launch": nbytes}
     value = at_peak / (ms_per_step / 1e3)
 
     # Dominant kernel's roofline (the one with the larger share of the step).
@@ -305,6 +348,12 @@ def main():
                 "achieved": parts[dom]["tflops"], "peak": PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s",
                 "frac": round(parts[dom]["tflops"] * 1e12 / PEAK_BF16_FLOPS, 4),
                 "traffic": measured_traffic(args.workload, "prefill_bf16_kernel", src), "source_hash": src}
+    elif dom == "append":
+        src = kernel_source_hash(["kv_append.hip", "device_common.h"])
+        roof = {"kernel": "kv_append_kernel", "bound": "hbm", "achieved": parts["append"]["gbps"],
+                "peak": PEAK_HBM_BYTES / 1e9, "unit": "GB/s",
+                "frac": round(parts["append"]["gbps"] * 1e9 / PEAK_HBM_BYTES, 4),
+                "traffic": measured_traffic(args.workload, "kv_append_kernel", src), "source_hash": src}
     else:
         src = kernel_source_hash(["decode_paged.hip", "device_common.h"])
         roof = {"kernel": "decode_stream_kernel+decode_combine_kernel", "bound": "hbm",
@@ -319,6 +368,9 @@ def main():
     if dec_inputs is not None:
         cfg["seed_decode"] = 100 + args.workload
         cfg["decode_tokens"] = int(dec_inputs.seq_lens.sum())
+    if app_in is not None:
+        cfg["seed_append"] = args.workload
+        cfg["append_seq_lens"] = app_in.seq_lens.tolist()
     if chunk_in is not None:
         cfg["seed_chunk"] = args.workload
         cfg["chunk_seq_lens"] = chunk_in.seq_lens.tolist()
@@ -338,6 +390,8 @@ def main():
         result["cpu_baseline"] = cpu_baseline(pre_inputs, pre_shape, dec_inputs)
     if not args.no_cpu_baseline and args.workload == 6:
         result["cpu_baseline"] = cpu_baseline_chunk(chunk_in)
+    if not args.no_cpu_baseline and args.workload == 7:
+        result["cpu_baseline"] = cpu_baseline_append(app_in)
     print(json.dumps(result), flush=True)
 
 
