@@ -28,5 +28,6 @@ from .attention import (  # noqa: F401
     kv_head_of,
     prefill,
     prefill_paged,
+    prefill_varlen,
     prefill_rows,
 )

@@ -36,6 +36,12 @@ design notes of the repository):
   is the case Tq = 1; a chunk that is the whole sequence (L = Tq) is the
   dense prefill above.
 
+  Ragged (varlen) batched prefill: several sequences of different lengths
+  packed token after token in one tensor, sequence s holding tokens
+  cu_seqlens[s] .. cu_seqlens[s+1]-1; each is an independent causal prefill
+  (no token sees another sequence) (ragged / varlen prefill of the
+  RoseLLM README, "Systems highlights", "Inference and serving").
+
   Paged decode: one query per sequence, standing at position L-1 of a
   sequence of L = seq_lens[b] cached tokens, so it sees keys 0..L-1 (its own
   K/V already appended).  Token j lives in physical page
@@ -248,3 +254,35 @@ def kv_append(k_pages, v_pages, k_new, v_new, block_table, seq_lens, page_size):
             k_out[page, :, position % page_size] = np.asarray(k_new)[b, :, t]
             v_out[page, :, position % page_size] = np.asarray(v_new)[b, :, t]
     return k_out, v_out
+
+
+def prefill_varlen(q, k, v, cu_seqlens, scale):
+    """Causal prefill of a ragged batch packed along the token axis.
+
+    q [N, Hq, d], k/v [N, Hkv, d] with N = cu_seqlens[-1]; cu_seqlens [S+1]
+    non-decreasing from 0.  Token i of sequence s (packed index
+    cu_seqlens[s] + i) sees keys cu_seqlens[s] .. cu_seqlens[s] + i.
+    Returns (out [N, Hq, d], lse [N, Hq]).
+    """
+    q, k, v = _as64(q), _as64(k), _as64(v)
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    if q.ndim != 3 or k.ndim != 3 or k.shape != v.shape or q.shape[0] != k.shape[0] or q.shape[2] != k.shape[2]:
+        raise ValueError("q must be [N, Hq, d] and k, v [N, Hkv, d]")
+    N, Hq, d = q.shape
+    Hkv = k.shape[1]
+    kv_head_of(0, Hq, Hkv)
+    if cu.ndim != 1 or cu.size < 1 or cu[0] != 0 or cu[-1] != N or np.any(np.diff(cu) < 0):
+        raise ValueError("cu_seqlens must rise from 0 to N")
+    out = np.zeros((N, Hq, d))
+    lse = np.zeros((N, Hq))
+    for s in range(cu.size - 1):
+        first, last = int(cu[s]), int(cu[s + 1])
+        n = last - first
+        if n == 0:
+            continue
+        seen = np.tril(np.ones((n, n), dtype=bool))
+        for h in range(Hq):
+            g = kv_head_of(h, Hq, Hkv)
+            o, l = _attend(q[first:last, h], k[first:last, g], v[first:last, g], float(scale), seen)
+            out[first:last, h], lse[first:last, h] = o, l
+    return out, lse

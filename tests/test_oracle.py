@@ -414,6 +414,73 @@ def test_append_then_decode_equals_dense_history():
     np.testing.assert_allclose(ld, lp[:, :, L - 1], rtol=0, atol=1e-13)
 
 
+# ---------------------------------------------------------------- ragged (varlen) prefill
+def varlen_case(seed, lens, Hq=4, Hkv=2, d=3):
+    r = rng(seed)
+    N = sum(lens)
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    return r.standard_normal((N, Hq, d)) * 2.0, r.standard_normal((N, Hkv, d)), r.standard_normal((N, Hkv, d)), cu
+
+
+def test_varlen_single_sequence_is_sdpa():
+    """One packed sequence against torch's float64 SDPA (an independent library routine)."""
+    q, k, v, cu = varlen_case(50, [9], Hq=4, Hkv=2, d=5)
+    out, lse = oracle.prefill_varlen(q, k, v, cu, 0.45)
+    qt = torch.from_numpy(q).permute(1, 0, 2)[None]
+    kt = torch.from_numpy(k).permute(1, 0, 2)[None]
+    vt = torch.from_numpy(v).permute(1, 0, 2)[None]
+    ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, is_causal=True, scale=0.45, enable_gqa=True)
+    np.testing.assert_allclose(out, ref[0].permute(1, 0, 2).numpy(), rtol=0, atol=1e-13)
+
+
+def test_varlen_sequences_do_not_see_each_other():
+    """Changing one sequence's keys and values leaves every other sequence bitwise unchanged;
+    the packed result equals each sequence computed alone (empty sequences included)."""
+    lens = [5, 0, 8, 1, 6]
+    q, k, v, cu = varlen_case(51, lens)
+    out, lse = oracle.prefill_varlen(q, k, v, cu, 0.7)
+    k2, v2 = k.copy(), v.copy()
+    k2[cu[2] : cu[3]] += 3.0
+    v2[cu[2] : cu[3]] -= 1.0
+    out2, lse2 = oracle.prefill_varlen(q, k2, v2, cu, 0.7)
+    other = np.ones(q.shape[0], dtype=bool)
+    other[cu[2] : cu[3]] = False
+    np.testing.assert_array_equal(out2[other], out[other])
+    np.testing.assert_array_equal(lse2[other], lse[other])
+    assert not np.allclose(out2[~other], out[~other])
+    for s in range(len(lens)):
+        a, b = cu[s], cu[s + 1]
+        o1, l1 = oracle.prefill_varlen(q[a:b], k[a:b], v[a:b], np.array([0, b - a]), 0.7)
+        np.testing.assert_allclose(out[a:b], o1, rtol=0, atol=1e-13)
+        np.testing.assert_allclose(lse[a:b], l1, rtol=0, atol=1e-13)
+
+
+def test_varlen_zero_query_is_prefix_mean():
+    lens = [3, 7]
+    q, k, v, cu = varlen_case(52, lens, Hq=4, Hkv=2)
+    v[:, 1] += 4.0
+    out, lse = oracle.prefill_varlen(np.zeros_like(q), k, v, cu, 0.9)
+    for s in range(2):
+        for i in range(lens[s]):
+            t = cu[s] + i
+            for h in range(4):
+                np.testing.assert_allclose(out[t, h], v[cu[s] : t + 1, h // 2].mean(axis=0), rtol=0, atol=1e-13)
+                assert abs(lse[t, h] - math.log(i + 1)) < 1e-13
+
+
+def test_varlen_brute_force():
+    lens = [2, 4]
+    q, k, v, cu = varlen_case(53, lens, Hq=2, Hkv=1, d=2)
+    out, lse = oracle.prefill_varlen(q, k, v, cu, 0.8)
+    for s in range(2):
+        for i in range(lens[s]):
+            t = cu[s] + i
+            for h in range(2):
+                o, l = _mp_attention_row(q[t, h], k[cu[s] : t + 1, 0], v[cu[s] : t + 1, 0], 0.8)
+                np.testing.assert_allclose(out[t, h], o, rtol=0, atol=1e-14)
+                assert abs(lse[t, h] - l) < 1e-13
+
+
 # ---------------------------------------------------------------- golden closed forms
 def _read_fixture(name):
     header, rows, cols = {}, [], None

@@ -62,6 +62,10 @@ MUTATIONS = {
         ("page = int(bt[b, position // page_size])", "page = int(bt[b, position % page_size])"),
         ("k_out[page, :, position % page_size]", "k_out[page, :, position // page_size]"),
     ],
+    "varlen keys from the batch start": [("_attend(q[first:last, h], k[first:last, g], v[first:last, g]",
+                                          "_attend(q[first:last, h], k[:n, g], v[:n, g]")],
+    "varlen mask not causal": [("seen = np.tril(np.ones((n, n), dtype=bool))", "seen = np.ones((n, n), dtype=bool)")],
+    "varlen heads taken modulo": [("g = kv_head_of(h, Hq, Hkv)", "g = h % Hkv")],
     "append writes V into K": [("k_out[page, :, position % page_size] = np.asarray(k_new)[b, :, t]",
                                 "k_out[page, :, position % page_size] = np.asarray(v_new)[b, :, t]")],
 }
