@@ -1,5 +1,5 @@
-"""Causal MHA/GQA attention for MI355X (gfx950): bf16 MFMA prefill (dense, or chunked over a paged
-cache) and paged split-KV decode.
+"""Causal MHA/GQA attention for MI355X (gfx950): bf16 MFMA prefill (dense, ragged over packed tokens, or
+chunked over a paged cache), paged split-KV decode, and the paged-cache KV append.
 
 The compute lives in ``libattn.so`` (hand-written HIP kernels behind the C ABI
 declared in ``include/attn.h``); this package is its ctypes binding, with the
@@ -24,8 +24,10 @@ from ._binding import (  # noqa: F401
     attn_last_error_message,
     attn_prefill,
     attn_prefill_paged,
+    attn_prefill_varlen,
     attn_status_string,
     attn_validate_chunk_metadata,
     attn_validate_paged_metadata,
+    attn_validate_varlen_metadata,
     load_library,
 )

@@ -53,6 +53,10 @@ def load_library():
     lib.attn_prefill_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, f32, i32,
                                        vp]
     lib.attn_prefill_paged.restype = i32
+    lib.attn_prefill_varlen.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32, vp]
+    lib.attn_prefill_varlen.restype = i32
+    lib.attn_validate_varlen_metadata.argtypes = [vp, i32, i32, i32]
+    lib.attn_validate_varlen_metadata.restype = i32
     lib.attn_kv_append.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, vp]
     lib.attn_kv_append.restype = i32
     lib.attn_validate_chunk_metadata.argtypes = [vp, vp, i32, i32, i32, i32, i32]
@@ -176,6 +180,36 @@ def attn_prefill_paged(q, k_pages, v_pages, block_table, seq_lens, out=None, lse
     return out, (None if lse is False else lse)
 
 
+def attn_prefill_varlen(q, k, v, cu_seqlens, max_seqlen, out=None, lse=None, scale=None, stream=None):
+    """Causal prefill of a ragged batch packed along tokens.  q [N,Hq,d], k/v [N,Hkv,d], cu_seqlens [S+1] int32
+    (device), max_seqlen (host int) -> (out [N,Hq,d], lse fp32 [N,Hq])."""
+    torch = _torch()
+    _require(q.dim() == 3 and k.dim() == 3 and k.shape == v.shape, "q must be [N, Hq, d] and k, v [N, Hkv, d]")
+    N, Hq, d = q.shape
+    Hkv = k.shape[1]
+    _require(k.shape[0] == N and k.shape[2] == d, "k/v shape mismatch")
+    _require(cu_seqlens.dim() == 1 and cu_seqlens.numel() >= 1 and cu_seqlens.dtype == torch.int32,
+             "cu_seqlens must be int32 [num_seqs + 1]")
+    for n, t in (("q", q), ("k", k), ("v", v), ("cu_seqlens", cu_seqlens)):
+        _dense_on_gpu(n, t)
+    _require(q.dtype == k.dtype == v.dtype, "q, k, v must share a dtype")
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((N, Hq), dtype=torch.float32, device=q.device)
+    _dense_on_gpu("out", out)
+    _require(out.shape == q.shape and out.dtype == q.dtype, "out must match q")
+    if lse is not False:
+        _dense_on_gpu("lse", lse)
+        _require(lse.shape == (N, Hq) and lse.dtype == torch.float32, "lse must be float32 [N, Hq]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    _check(load_library().attn_prefill_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(out), None if lse is False else _ptr(lse),
+                                              _ptr(cu_seqlens), cu_seqlens.numel() - 1, N, int(max_seqlen), Hq, Hkv,
+                                              d, float(scale), _dtype_code(q), _stream(stream)))
+    return out, (None if lse is False else lse)
+
+
 def attn_kv_append(k_new, v_new, k_pages, v_pages, block_table, seq_lens, stream=None):
     """Write the last Tn tokens of each sequence into the paged cache, in place.  k_new/v_new [B,Hkv,Tn,d];
     pools [P,Hkv,page,d]; block_table [B,W] int32; seq_lens [B] int32 = lengths after the append (>= Tn)."""
@@ -268,3 +302,12 @@ def attn_validate_chunk_metadata(block_table, seq_lens, page_size, num_pages, ch
     B, W = bt.shape
     _check(load_library().attn_validate_chunk_metadata(bt.ctypes.data, sl.ctypes.data, B, W, page_size, num_pages,
                                                        chunk_len))
+
+
+def attn_validate_varlen_metadata(cu_seqlens, total_tokens, max_seqlen):
+    """Host check of cu_seqlens (CPU int32 tensor or array) for attn_prefill_varlen; raises AttnError."""
+    import numpy as np
+
+    cu = np.ascontiguousarray(np.asarray(cu_seqlens.cpu() if hasattr(cu_seqlens, "cpu") else cu_seqlens,
+                                         dtype=np.int32))
+    _check(load_library().attn_validate_varlen_metadata(cu.ctypes.data, cu.size - 1, total_tokens, max_seqlen))

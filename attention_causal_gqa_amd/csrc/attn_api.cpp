@@ -183,6 +183,56 @@ int attn_prefill_paged(const void* q, const void* k_pages, const void* v_pages, 
                     "attn_prefill_paged launch");
 }
 
+int attn_prefill_varlen(const void* q, const void* k, const void* v, void* out, float* lse, const int32_t* cu_seqlens,
+                        int num_seqs, int total_tokens, int max_seqlen, int Hq, int Hkv, int d, float scale,
+                        attn_dtype_t dtype, hipStream_t stream) {
+    g_last_error.clear();
+    if (dtype != ATTN_F32 && dtype != ATTN_BF16) return fail(ATTN_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
+    if (num_seqs < 0 || total_tokens < 0 || max_seqlen < 0)
+        return fail(ATTN_ERR_INVALID_ARG, "num_seqs=%d, total_tokens=%d, max_seqlen=%d must be >= 0", num_seqs,
+                    total_tokens, max_seqlen);
+    if (Hq < 1 || Hkv < 1) return fail(ATTN_ERR_INVALID_ARG, "Hq=%d, Hkv=%d must be >= 1", Hq, Hkv);
+    if (Hq % Hkv != 0) return fail(ATTN_ERR_INVALID_ARG, "Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
+    if (d < 1) return fail(ATTN_ERR_INVALID_ARG, "d=%d must be >= 1", d);
+    if (!std::isfinite(scale)) return fail(ATTN_ERR_INVALID_ARG, "scale must be finite");
+    if (dtype != ATTN_BF16) return fail(ATTN_ERR_UNSUPPORTED, "ragged prefill supports ATTN_BF16 only");
+    if (d != 64 && d != 128) return fail(ATTN_ERR_UNSUPPORTED, "ragged prefill supports d = 64 or 128, not %d", d);
+    if (Hq / Hkv > kMaxPrefillGroup)
+        return fail(ATTN_ERR_UNSUPPORTED, "ragged prefill supports Hq/Hkv <= %d", kMaxPrefillGroup);
+    if (num_seqs == 0 || total_tokens == 0 || max_seqlen == 0) return ATTN_OK;
+    if (!q || !k || !v || !out || !cu_seqlens)
+        return fail(ATTN_ERR_INVALID_ARG, "q, k, v, out and cu_seqlens must be non-null");
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16))
+        return fail(ATTN_ERR_INVALID_ARG, "q, k, v and out must be 16-byte aligned");
+    if (!aligned(cu_seqlens, 4) || (lse && !aligned(lse, 4)))
+        return fail(ATTN_ERR_INVALID_ARG, "cu_seqlens and lse must be 4-byte aligned");
+    const int64_t rows_per_block = 256 / (Hq / Hkv);
+    const int64_t blocks = (max_seqlen + rows_per_block - 1) / rows_per_block * num_seqs * Hkv;
+    if (blocks > kMaxGrid) return fail(ATTN_ERR_INVALID_ARG, "problem too large: %lld workgroups", (long long)blocks);
+
+    attn::PrefillArgs a{q, k, v, out, lse, num_seqs, Hq, Hkv, max_seqlen, d, scale};
+    return from_hip(attn::launch_prefill_varlen_bf16(a, cu_seqlens, stream), "attn_prefill_varlen launch");
+}
+
+int attn_validate_varlen_metadata(const int32_t* cu_seqlens_host, int num_seqs, int total_tokens, int max_seqlen) {
+    g_last_error.clear();
+    if (num_seqs < 0 || total_tokens < 0 || max_seqlen < 0)
+        return fail(ATTN_ERR_INVALID_ARG, "bad sizes: num_seqs=%d total_tokens=%d max_seqlen=%d", num_seqs,
+                    total_tokens, max_seqlen);
+    if (!cu_seqlens_host) return fail(ATTN_ERR_INVALID_ARG, "null cu_seqlens");
+    if (cu_seqlens_host[0] != 0) return fail(ATTN_ERR_INVALID_ARG, "cu_seqlens[0]=%d must be 0", cu_seqlens_host[0]);
+    for (int s = 0; s < num_seqs; ++s) {
+        const int64_t n = (int64_t)cu_seqlens_host[s + 1] - cu_seqlens_host[s];
+        if (n < 0 || n > max_seqlen)
+            return fail(ATTN_ERR_INVALID_ARG, "sequence %d has %lld tokens, outside [0, max_seqlen=%d]", s, (long long)n,
+                        max_seqlen);
+    }
+    if (cu_seqlens_host[num_seqs] != total_tokens)
+        return fail(ATTN_ERR_INVALID_ARG, "cu_seqlens[%d]=%d must equal total_tokens=%d", num_seqs,
+                    cu_seqlens_host[num_seqs], total_tokens);
+    return ATTN_OK;
+}
+
 int attn_kv_append(const void* k_new, const void* v_new, void* k_pages, void* v_pages, const int32_t* block_table,
                    const int32_t* seq_lens, int B, int Hkv, int Tn, int d, int page_size, int num_pages,
                    int max_pages_per_seq, attn_dtype_t dtype, hipStream_t stream) {

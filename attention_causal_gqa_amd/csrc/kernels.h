@@ -49,6 +49,10 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream);
 // [num_pages, Hkv, 16, d], a.T is the chunk length; block_table [B, W].
 hipError_t launch_prefill_paged_bf16(const PrefillArgs& a, const int32_t* block_table, const int32_t* seq_lens, int W,
                                      hipStream_t stream);
+// Ragged batch packed along the token axis: a.q / a.out [N, Hq, d], a.k / a.v
+// [N, Hkv, d], a.lse [N, Hq]; a.B sequences, cu_seqlens [B+1]; a.T is the
+// longest sequence.
+hipError_t launch_prefill_varlen_bf16(const PrefillArgs& a, const int32_t* cu_seqlens, hipStream_t stream);
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_kv_append_bf16(const KvAppendArgs& a, hipStream_t stream);
 

@@ -53,6 +53,10 @@ constexpr int kBN = 64;     // keys per tile
 constexpr int kPage = 16;   // tokens per page of a paged cache
 constexpr int kMaxTablePages = 8192;  // block-table entries staged in LDS (contexts up to 131072 tokens)
 
+// Forms of the prefill kernel: dense [B, H, T, d] tensors; chunked prefill
+// over a paged cache; a ragged batch packed along the token axis.
+enum PrefillMode { kDense = 0, kPagedMode = 1, kVarlenMode = 2 };
+
 // XOR swizzle of 16-byte chunks within an LDS row of CPR chunks: chunk c of
 // row r is stored at position c ^ swz(r).  With CPR = 16 (256-byte rows),
 // swz(r) = 4(r%4) + (r/4)%4: 16 consecutive rows read at one chunk (the K
@@ -110,14 +114,21 @@ __device__ __forceinline__ void dma16(const void* g, char* lds_base) {
 // read in slots 2t-2 and 2t-1; A waits for it before the barrier that ends
 // slot 2t+1.
 //
-// kPaged: chunked prefill over a paged cache.  k and v are then page pools
+// kMode == kVarlenMode: a ragged batch packed along the token axis
+// (q, out [N, Hq, d], k, v [N, Hkv, d], lse [N, Hq]); sequence b holds
+// tokens cu[b] .. cu[b+1]-1 (cu is passed as seq_lens) and T is the longest
+// sequence.  A workgroup whose query block lies past its sequence's end
+// exits before touching memory; rows and keys are read with the token-major
+// strides Hq*d and Hkv*d.
+//
+// kMode == kPagedMode: chunked prefill over a paged cache.  k and v are then page pools
 // [num_pages, Hkv, 16, D]; the T queries of sequence b are its last T
 // tokens, so query t stands at position pos0 + t with pos0 = seq_lens[b] - T
 // and sees keys 0 .. pos0 + t (the causal mask aligned to the bottom-right
 // corner).  The block-table entries the workgroup needs are staged in LDS
 // once; each DMA row then finds its page there.  With pos0 = 0 and dense
 // K/V this is the plain prefill.
-template <int D, bool kPosScale, bool kPaged>
+template <int D, bool kPosScale, int kMode>
 __global__ __launch_bounds__(512, 1) void prefill_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                                                               const bf16* __restrict__ v, bf16* __restrict__ out,
                                                               float* __restrict__ lse, int B, int Hq, int Hkv, int T,
@@ -144,6 +155,8 @@ __global__ __launch_bounds__(512, 1) void prefill_bf16_kernel(const bf16* __rest
     // compiler wait for all LDS reads at every LDS wait inside the loop,
     // because scalar loads can complete out of order.
     __asm__ volatile("" ::"s"(q), "s"(k), "s"(v), "s"(out), "s"(lse), "s"(block_table), "s"(seq_lens));
+    constexpr bool kPaged = kMode == kPagedMode;
+    constexpr bool kVarlen = kMode == kVarlenMode;
     __shared__ int bt_lds[kPaged ? kMaxTablePages : 1];  // the sequence's block table (paged form)
 
     const int tid = threadIdx.x;
@@ -159,26 +172,31 @@ __global__ __launch_bounds__(512, 1) void prefill_bf16_kernel(const bf16* __rest
     const int b = pair / Hkv;
     const int kvh = pair % Hkv;
     const int t0 = qb * BMt;
-    // Keys of the sequence (Lkv) and the position of query 0 (pos0).
-    int Lkv = T, pos0 = 0;
-    if constexpr (kPaged) {
-        Lkv = seq_lens[b];
-        pos0 = Lkv - T;
+    // Queries of this sequence (Tb), the position of query 0 (pos0), and in
+    // the packed form the sequence's first token (tok0).
+    int Tb = T, pos0 = 0;
+    size_t tok0 = 0;
+    if constexpr (kPaged) pos0 = seq_lens[b] - T;
+    if constexpr (kVarlen) {
+        tok0 = (size_t)seq_lens[b];
+        Tb = seq_lens[b + 1] - seq_lens[b];
+        if (t0 >= Tb) return;  // the whole workgroup, before any barrier
     }
-    const int kend = pos0 + min(t0 + BMt, T);  // keys 0..kend-1 are visible to some row
+    const int kend = pos0 + min(t0 + BMt, Tb);  // keys 0..kend-1 are visible to some row
 
     // This lane's query column: row r of the workgroup (256 rows).
     const int r = 32 * w + l32;
     const int tt = r / G;
     const int head = kvh * G + (r % G);
     const int token = t0 + tt;
-    const bool row_ok = tt < BMt && token < T;
+    const bool row_ok = tt < BMt && token < Tb;
     const int token_ld = row_ok ? token : t0;  // dead rows compute on a valid row, never stored
 
     // Q^T as the B operand: lane holds Q[row][16kk + 8hi .. +7].
     bf16x8 qreg[NKK];
     {
-        const bf16* qrow = q + ((size_t)(b * Hq + head) * T + token_ld) * D + 8 * hi;
+        const bf16* qrow = (kVarlen ? q + ((tok0 + token_ld) * Hq + head) * D
+                                    : q + ((size_t)(b * Hq + head) * T + token_ld) * D) + 8 * hi;
 #pragma unroll
         for (int kk = 0; kk < NKK; ++kk) qreg[kk] = *reinterpret_cast<const bf16x8*>(qrow + 16 * kk);
     }
@@ -187,8 +205,13 @@ __global__ __launch_bounds__(512, 1) void prefill_bf16_kernel(const bf16* __rest
     // i.e. rows RPI*n .. RPI*n + RPI-1; lane l lands at row RPI*n + l / CPR,
     // swizzled position l % CPR, so it fetches logical chunk (l % CPR) ^ swz(row).
     // Wave w owns DMAs w*NIW .. w*NIW + NIW-1 of every tile.
-    const bf16* kbase = kPaged ? k + (size_t)kvh * kPage * D : k + (size_t)(b * Hkv + kvh) * T * D;
-    const bf16* vbase = kPaged ? v + (size_t)kvh * kPage * D : v + (size_t)(b * Hkv + kvh) * T * D;
+    const bf16* kbase = kPaged    ? k + (size_t)kvh * kPage * D
+                        : kVarlen ? k + (tok0 * Hkv + kvh) * D
+                                  : k + (size_t)(b * Hkv + kvh) * T * D;
+    const bf16* vbase = kPaged    ? v + (size_t)kvh * kPage * D
+                        : kVarlen ? v + (tok0 * Hkv + kvh) * D
+                                  : v + (size_t)(b * Hkv + kvh) * T * D;
+    const uint32_t krs = kVarlen ? (uint32_t)(Hkv * ROWB) : (uint32_t)ROWB;  // bytes between consecutive keys
     // Group A (waves 0-3) issues every DMA: wave w takes the DMAs of wave
     // slots w and w + 4, i.e. DMAs w*NIW .. and (w+4)*NIW .. of every tile.
     constexpr int NDW = 2 * NIW;
@@ -199,13 +222,13 @@ __global__ __launch_bounds__(512, 1) void prefill_bf16_kernel(const bf16* __rest
     for (int j = 0; j < NDW; ++j) {
         dslot[j] = ((w & 3) + 4 * (j / NIW)) * NIW + j % NIW;
         drow[j] = RPI * dslot[j] + lane / CPR;
-        doff[j] = (uint32_t)(drow[j] * ROWB + 16 * ((lane % CPR) ^ swz<CPR>(drow[j])));
+        doff[j] = (uint32_t)(drow[j] * krs + 16 * ((lane % CPR) ^ swz<CPR>(drow[j])));
     }
-    // Keys at or past kend (the paged form) or T (the dense form) are read
-    // as the last one before it: they are masked for every row of the
-    // workgroup (their positions are below kend), and V is finite, so they
-    // add exact zeros.  The paged form must not go past kend - 1: only the
-    // block-table entries of keys 0..kend-1 are staged.
+    // Keys at or past kend (the paged form) or Tb (the dense and packed
+    // forms) are read as the last one before it: they are masked for every
+    // row of the workgroup (their positions are below kend), and V is
+    // finite, so they add exact zeros.  The paged form must not go past
+    // kend - 1: only the block-table entries of keys 0..kend-1 are staged.
     auto dma_tile = [&](const bf16* base, char* dst, int k0) __attribute__((always_inline)) {
         if constexpr (kPaged) {
             // (page, kv head) slices are kPage rows of ROWB bytes, Hkv slices per page.
@@ -217,16 +240,16 @@ __global__ __launch_bounds__(512, 1) void prefill_bf16_kernel(const bf16* __rest
                 dma16(bb + (page * Hkv * kPage + key % kPage) * ROWB + (doff[j] - (uint32_t)(drow[j] * ROWB)),
                       dst + 1024 * dslot[j]);
             }
-        } else if (k0 + kBN <= T) {
-            const char* tb = reinterpret_cast<const char*>(base + (size_t)k0 * D);
+        } else if (k0 + kBN <= Tb) {
+            const char* tb = reinterpret_cast<const char*>(base) + (size_t)k0 * krs;
 #pragma unroll
             for (int j = 0; j < NDW; ++j) dma16(tb + doff[j], dst + 1024 * dslot[j]);
         } else {
             const char* bb = reinterpret_cast<const char*>(base);
 #pragma unroll
             for (int j = 0; j < NDW; ++j) {
-                const int key = min(k0 + drow[j], T - 1);
-                dma16(bb + (size_t)key * ROWB + (doff[j] - (uint32_t)(drow[j] * ROWB)), dst + 1024 * dslot[j]);
+                const int key = min(k0 + drow[j], Tb - 1);
+                dma16(bb + (size_t)key * krs + (doff[j] - (uint32_t)drow[j] * krs), dst + 1024 * dslot[j]);
             }
         }
     };
@@ -466,7 +489,8 @@ __global__ __launch_bounds__(512, 1) void prefill_bf16_kernel(const bf16* __rest
     const float ll = pair_sum(l_lse);
     if (row_ok) {
         const float inv = 1.f / lt;
-        bf16* orow = out + ((size_t)(b * Hq + head) * T + token) * D + 4 * hi;
+        bf16* orow = (kVarlen ? out + ((tok0 + token) * Hq + head) * D
+                              : out + ((size_t)(b * Hq + head) * T + token) * D) + 4 * hi;
         // O^T element i of block mb is d = 32mb + 8(i/4) + 4hi + i%4.
 #pragma unroll
         for (int mb = 0; mb < NMB; ++mb)
@@ -476,11 +500,12 @@ __global__ __launch_bounds__(512, 1) void prefill_bf16_kernel(const bf16* __rest
                                   pack_bf16x2(oacc[mb][4 * g4 + 2] * inv, oacc[mb][4 * g4 + 3] * inv)};
                 *reinterpret_cast<u32x2*>(orow + 32 * mb + 8 * g4) = wv;
             }
-        if (lse != nullptr && hi == 0) lse[(size_t)(b * Hq + head) * T + token] = (m_run + log2f(ll)) * kLn2;
+        if (lse != nullptr && hi == 0)
+            lse[kVarlen ? (tok0 + token) * Hq + head : (size_t)(b * Hq + head) * T + token] = (m_run + log2f(ll)) * kLn2;
     }
 }
 
-template <int D, bool kPaged>
+template <int D, int kMode>
 hipError_t launch_d(const PrefillArgs& a, const int* block_table, const int* seq_lens, int W, hipStream_t stream) {
     const int G = a.Hq / a.Hkv;
     const int BMt = kRows / G;
@@ -488,11 +513,11 @@ hipError_t launch_d(const PrefillArgs& a, const int* block_table, const int* seq
     const dim3 grid((unsigned)nqb * a.B * a.Hkv);
     const float c1 = (float)((double)a.scale * 1.4426950408889634);
     if (c1 > 0.f) {
-        hipLaunchKernelGGL((prefill_bf16_kernel<D, true, kPaged>), grid, dim3(512), 0, stream, (const bf16*)a.q,
+        hipLaunchKernelGGL((prefill_bf16_kernel<D, true, kMode>), grid, dim3(512), 0, stream, (const bf16*)a.q,
                            (const bf16*)a.k, (const bf16*)a.v, (bf16*)a.out, a.lse, a.B, a.Hq, a.Hkv, a.T, G, BMt,
                            nqb, c1, block_table, seq_lens, W);
     } else {
-        hipLaunchKernelGGL((prefill_bf16_kernel<D, false, kPaged>), grid, dim3(512), 0, stream, (const bf16*)a.q,
+        hipLaunchKernelGGL((prefill_bf16_kernel<D, false, kMode>), grid, dim3(512), 0, stream, (const bf16*)a.q,
                            (const bf16*)a.k, (const bf16*)a.v, (bf16*)a.out, a.lse, a.B, a.Hq, a.Hkv, a.T, G, BMt,
                            nqb, c1, block_table, seq_lens, W);
     }
@@ -502,14 +527,19 @@ hipError_t launch_d(const PrefillArgs& a, const int* block_table, const int* seq
 }  // namespace
 
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream) {
-    return a.d == 128 ? launch_d<128, false>(a, nullptr, nullptr, 0, stream)
-                      : launch_d<64, false>(a, nullptr, nullptr, 0, stream);
+    return a.d == 128 ? launch_d<128, kDense>(a, nullptr, nullptr, 0, stream)
+                      : launch_d<64, kDense>(a, nullptr, nullptr, 0, stream);
 }
 
 hipError_t launch_prefill_paged_bf16(const PrefillArgs& a, const int32_t* block_table, const int32_t* seq_lens, int W,
                                      hipStream_t stream) {
-    return a.d == 128 ? launch_d<128, true>(a, block_table, seq_lens, W, stream)
-                      : launch_d<64, true>(a, block_table, seq_lens, W, stream);
+    return a.d == 128 ? launch_d<128, kPagedMode>(a, block_table, seq_lens, W, stream)
+                      : launch_d<64, kPagedMode>(a, block_table, seq_lens, W, stream);
+}
+
+hipError_t launch_prefill_varlen_bf16(const PrefillArgs& a, const int32_t* cu_seqlens, hipStream_t stream) {
+    return a.d == 128 ? launch_d<128, kVarlenMode>(a, nullptr, cu_seqlens, 0, stream)
+                      : launch_d<64, kVarlenMode>(a, nullptr, cu_seqlens, 0, stream);
 }
 
 }  // namespace attn

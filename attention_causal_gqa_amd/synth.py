@@ -77,6 +77,40 @@ def chunk_flops(Hq, d, Tq, seq_lens) -> int:
     return 4 * Hq * d * pairs
 
 
+@dataclass(frozen=True)
+class VarlenShape:
+    """Ragged prefill: S sequences of T ~ U{T_lo..T_hi} tokens packed along the token axis."""
+    S: int
+    Hq: int
+    Hkv: int
+    d: int
+    T_lo: int
+    T_hi: int
+    dtype: torch.dtype
+
+
+def varlen_flops(Hq, d, lens) -> int:
+    """Algorithmic flops of a ragged prefill: each sequence's causal triangle, diagonal included."""
+    return sum(2 * Hq * d * int(T) * (int(T) + 1) for T in lens)
+
+
+def varlen_inputs(shape: VarlenShape, seed: int, *, lens=None):
+    """q [N,Hq,d], k, v [N,Hkv,d] (CPU), cu_seqlens int32 [S+1] and max_seqlen.
+
+    Draw order: lengths (unless given), then Q, K, V, iid N(0,1) rounded to shape.dtype."""
+    g = torch.Generator().manual_seed(seed)
+    if lens is None:
+        lens = torch.randint(shape.T_lo, shape.T_hi + 1, (shape.S,), generator=g)
+    lens = torch.as_tensor(lens, dtype=torch.int64)
+    N = int(lens.sum())
+    cu = torch.zeros(lens.numel() + 1, dtype=torch.int64)
+    cu[1:] = torch.cumsum(lens, 0)
+    q = torch.randn(N, shape.Hq, shape.d, generator=g).to(shape.dtype)
+    k = torch.randn(N, shape.Hkv, shape.d, generator=g).to(shape.dtype)
+    v = torch.randn(N, shape.Hkv, shape.d, generator=g).to(shape.dtype)
+    return q, k, v, cu.to(torch.int32), int(lens.max()) if lens.numel() else 0
+
+
 # The five workloads.  Prefill inputs are drawn with seed = workload number,
 # decode inputs with seed = 100 + workload number.
 WORKLOADS = {
@@ -96,6 +130,9 @@ WORKLOADS[6] = {"chunk": ChunkShape(4, 32, 8, 2048, 128, PAGE_SIZE, 4096, 16384,
 # KV append (seed 7): the 2048-token chunks of workload 6's shape written into the paged cache.
 WORKLOADS[7] = {"append": ChunkShape(4, 32, 8, 2048, 128, PAGE_SIZE, 4096, 16384, torch.bfloat16)}
 
+# Ragged prefill (seed 8): 16 sequences of 256..4096 tokens packed along the token axis.
+WORKLOADS[8] = {"varlen": VarlenShape(16, 32, 8, 128, 256, 4096, torch.bfloat16)}
+
 WORKLOAD_NAMES = {
     1: "causal MHA prefill fp32 B1 H4 T128 d64",
     2: "causal GQA prefill bf16 B1 Hq16 Hkv8 T512 d128",
@@ -104,6 +141,7 @@ WORKLOAD_NAMES = {
     5: "mixed: prefill bf16 B1 Hq32 Hkv8 T8192 d128 + paged decode bf16 B64 Hq32 Hkv8 d128 page16 L~U[1024,8192]",
     6: "chunked prefill bf16 over a paged cache B4 Hq32 Hkv8 Tq2048 d128 page16 L~U[4096,16384]",
     7: "KV append bf16 into a paged cache B4 Hkv8 Tn2048 d128 page16 L~U[4096,16384]",
+    8: "ragged prefill bf16 over packed tokens S16 Hq32 Hkv8 d128 T~U[256,4096]",
 }
 
 

@@ -26,6 +26,11 @@
  *    of the sequence's cached keys, causally.  It is the prefill kernel
  *    reading its key/value tiles page by page through the block table.
  *
+ *  - attn_prefill_varlen: causal prefill of a ragged batch, sequences of
+ *    different lengths packed token after token (ragged / varlen prefill,
+ *    RoseLLM README, "Systems highlights", "Inference and serving"); each
+ *    sequence is an independent causal prefill.
+ *
  *  - attn_kv_append: writes the newest tokens' keys and values into their
  *    slots of the paged cache (the KV-cache writer of the RoseLLM README,
  *    "Systems highlights", "Inference and serving"), the step before decode
@@ -127,6 +132,35 @@ int attn_prefill_paged(const void* q, const void* k_pages, const void* v_pages,
                        int B, int Hq, int Hkv, int Tq, int d, int page_size, int num_pages,
                        int max_pages_per_seq, float scale, attn_dtype_t dtype,
                        hipStream_t stream);
+
+/*
+ * Causal prefill of a ragged batch packed along the token axis.
+ *
+ *   q, out     : device, [total_tokens, Hq, d] in `dtype`
+ *   k, v       : device, [total_tokens, Hkv, d] in `dtype`
+ *   lse        : device, [total_tokens, Hq] float32, or NULL to skip it
+ *   cu_seqlens : device int32 [num_seqs + 1]: sequence s holds tokens
+ *                cu_seqlens[s] .. cu_seqlens[s+1]-1; cu_seqlens[0] = 0, the
+ *                entries do not decrease, cu_seqlens[num_seqs] = total_tokens
+ *   max_seqlen : >= every sequence's length (sizes the launch)
+ *   Hq, Hkv    : >= 1, Hq % Hkv == 0, Hq / Hkv <= 128
+ *   dtype      : ATTN_BF16; d = 128 or 64
+ * Token i of sequence s sees keys cu_seqlens[s] .. cu_seqlens[s] + i.
+ * num_seqs, total_tokens or max_seqlen equal to 0 enqueues nothing.
+ * cu_seqlens is read on the device only; values outside the contract above
+ * are undefined behaviour (check them with attn_validate_varlen_metadata).
+ * q, k, v must hold finite values.
+ */
+int attn_prefill_varlen(const void* q, const void* k, const void* v, void* out, float* lse,
+                        const int32_t* cu_seqlens, int num_seqs, int total_tokens, int max_seqlen,
+                        int Hq, int Hkv, int d, float scale, attn_dtype_t dtype, hipStream_t stream);
+
+/*
+ * Host-side check of a host copy of cu_seqlens against the contract of
+ * attn_prefill_varlen.  Returns ATTN_OK or ATTN_ERR_INVALID_ARG.
+ */
+int attn_validate_varlen_metadata(const int32_t* cu_seqlens_host, int num_seqs, int total_tokens,
+                                  int max_seqlen);
 
 /*
  * KV append: copy the last Tn tokens' keys and values of each sequence into

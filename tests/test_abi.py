@@ -27,7 +27,8 @@ def declared_functions():
 
 def test_header_declares_the_api():
     names = declared_functions()
-    for n in ("attn_prefill", "attn_prefill_paged", "attn_kv_append", "attn_decode_paged", "attn_decode_workspace_bytes",
+    for n in ("attn_prefill", "attn_prefill_paged", "attn_prefill_varlen", "attn_validate_varlen_metadata",
+              "attn_kv_append", "attn_decode_paged", "attn_decode_workspace_bytes",
               "attn_decode_num_splits", "attn_validate_paged_metadata", "attn_validate_chunk_metadata",
               "attn_status_string", "attn_last_error_message"):
         assert n in names
@@ -193,6 +194,45 @@ def test_kv_append_rejects(lib, kw, status):
 def test_kv_append_empty_is_a_no_op(lib):
     assert kv_append(lib, kn=None, vn=None, kp=None, vp=None, bt=None, sl=None, B=0) == A.ATTN_OK
     assert kv_append(lib, kn=None, vn=None, kp=None, vp=None, bt=None, sl=None, Tn=0) == A.ATTN_OK
+
+
+def prefill_varlen(lib, q=FAKE, k=FAKE, v=FAKE, out=FAKE, lse=None, cu=FAKE, S=3, N=100, Tmax=60, Hq=4, Hkv=2,
+                   d=128, scale=0.1, dtype=1):
+    return lib.attn_prefill_varlen(q, k, v, out, lse, cu, S, N, Tmax, Hq, Hkv, d, scale, dtype, None)
+
+
+@pytest.mark.parametrize(
+    "kw,status",
+    [
+        (dict(q=None), A.ATTN_ERR_INVALID_ARG),
+        (dict(cu=None), A.ATTN_ERR_INVALID_ARG),
+        (dict(v=FAKE + 8), A.ATTN_ERR_INVALID_ARG),
+        (dict(cu=FAKE + 2), A.ATTN_ERR_INVALID_ARG),
+        (dict(S=-1), A.ATTN_ERR_INVALID_ARG),
+        (dict(N=-1), A.ATTN_ERR_INVALID_ARG),
+        (dict(Hq=6, Hkv=4), A.ATTN_ERR_INVALID_ARG),
+        (dict(scale=float("nan")), A.ATTN_ERR_INVALID_ARG),
+        (dict(dtype=3), A.ATTN_ERR_INVALID_ARG),
+        (dict(dtype=0), A.ATTN_ERR_UNSUPPORTED),
+        (dict(d=256), A.ATTN_ERR_UNSUPPORTED),
+        (dict(Hq=256, Hkv=1), A.ATTN_ERR_UNSUPPORTED),
+    ],
+)
+def test_prefill_varlen_rejects(lib, kw, status):
+    assert prefill_varlen(lib, **kw) == status
+    assert A.attn_last_error_message() != ""
+
+
+def test_prefill_varlen_empty_is_a_no_op(lib):
+    for kw in (dict(S=0), dict(N=0, Tmax=0), dict(Tmax=0)):
+        assert prefill_varlen(lib, q=None, k=None, v=None, out=None, cu=None, **kw) == A.ATTN_OK
+
+
+def test_validate_varlen_metadata():
+    A.attn_validate_varlen_metadata(np.array([0, 3, 3, 10], dtype=np.int32), 10, 7)
+    for cu, N, T in (([1, 3, 10], 10, 7), ([0, 5, 3], 3, 7), ([0, 3, 10], 11, 7), ([0, 3, 11], 11, 7)):
+        with pytest.raises(A.AttnError):
+            A.attn_validate_varlen_metadata(np.array(cu, dtype=np.int32), N, T)
 
 
 def test_validate_chunk_metadata():
