@@ -16,11 +16,13 @@ GPU runs a short sleep kernel, so that the events time kernels rather than
 host launch latency.  A workload with a single part times its K queued
 launches between one pair of events instead (``ms_min`` stays per launch).
 
-    python bench.py [--steps K] [--warmup W] [--workload 5|3|4|6|7] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--workload 5|3|4|6|7|8] [--no-cpu-baseline]
 
 Workload 6 (not the default) times the chunked prefill over a paged cache:
 2048-token chunks at the end of four sequences of 4096..16384 cached tokens.
 Workload 7 times the KV append that writes such chunks into the cache.
+Workload 8 times the ragged prefill of 16 sequences of 256..4096 tokens
+packed along the token axis.
     python bench.py --copy-calibration   # plain 1 GiB copy, reference for HBM byte counters
 """
 
@@ -52,7 +54,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workload", type=int, default=5, choices=(3, 4, 5, 6, 7))
+    p.add_argument("--workload", type=int, default=5, choices=(3, 4, 5, 6, 7, 8))
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--flush", action="store_true",
                    help="write a 512 MiB buffer before each step (outside the kernel events) to evict L2/MALL")
@@ -195,6 +197,33 @@ def cpu_baseline_append(inp):
             "append_gbps": nbytes / t / 1e9, "host_cpu_count": os.cpu_count()}
 
 
+def cpu_baseline_varlen(var_in, shape, budget_s=20.0):
+    """Time the fp64 oracle on a bounded sample of the ragged workload: whole sequences, shortest first."""
+    import oracle
+    from threadpoolctl import threadpool_info
+
+    threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    q, k, v, cu, _ = var_in
+    qn, kn, vn = (t.float().numpy() for t in (q, k, v))
+    cu = cu.numpy()
+    order = np.argsort(cu[1:] - cu[:-1])
+    scale = synth.fp32_scale(shape.d)
+    t0 = time.perf_counter()
+    done = []
+    for s in order:
+        if done and time.perf_counter() - t0 > budget_s:
+            break
+        a, b = int(cu[s]), int(cu[s + 1])
+        oracle.prefill_varlen(qn[a:b], kn[a:b], vn[a:b], np.array([0, b - a]), scale)
+        done.append(b - a)
+    t = time.perf_counter() - t0
+    flops = synth.varlen_flops(shape.Hq, shape.d, done)
+    return {"value": flops / t / PEAK_BF16_FLOPS, "unit": "fraction of MI355X roofline", "cores": threads,
+            "kind": "oracle",
+            "sample": f"fp64 oracle: {len(done)} of {len(order)} sequences, shortest first (lengths {done}; {t:.2f} s)",
+            "varlen_tflops": flops / t / 1e12, "host_cpu_count": os.cpu_count()}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -211,8 +240,9 @@ def main():
     dec_shape = wl.get("decode")
     chunk_shape = wl.get("chunk")
     app_shape = wl.get("append")
+    var_shape = wl.get("varlen")
 
-    pre_inputs = dec_inputs = chunk_in = app_in = None
+    pre_inputs = dec_inputs = chunk_in = app_in = var_in = None
     work = {}
     if pre_shape is not None:
         pre_inputs = synth.prefill_inputs(pre_shape, seed=args.workload)
@@ -247,6 +277,14 @@ def main():
         akn, avn, akp, avp, abt, asl = (t.to(dev) for t in (app_in.k_new, app_in.v_new, app_in.k_pages,
                                                             app_in.v_pages, app_in.block_table, app_in.seq_lens))
         work["append"] = lambda: A.attn_kv_append(akn, avn, akp, avp, abt, asl)
+    if var_shape is not None:
+        var_in = synth.varlen_inputs(var_shape, seed=args.workload)
+        vq, vk, vv, vcu = (t.to(dev) for t in var_in[:4])
+        vT = var_in[4]
+        vout = torch.empty_like(vq)
+        vlse = torch.empty(vq.shape[:2], dtype=torch.float32, device=dev)
+        vscale = synth.fp32_scale(var_shape.d)
+        work["varlen"] = lambda: A.attn_prefill_varlen(vq, vk, vv, vcu, vT, out=vout, lse=vlse, scale=vscale)
     flush_buf = torch.empty(512 << 20, dtype=torch.uint8, device=dev) if args.flush else None
 
     names = list(work)
@@ -331,6 +369,14 @@ def main():
         parts["chunk"] = {"ms": round(ms["chunk"], 4), "ms_min": round(min(per["chunk"]), 4),
                           "tflops": round(flops / t / 1e12, 1), "frac_of_peak": round(flops / t / PEAK_BF16_FLOPS, 4),
                           "flops_per_launch": flops}
+    if var_shape is not None:
+        lens = (var_in[3][1:] - var_in[3][:-1]).tolist()
+        flops = synth.varlen_flops(var_shape.Hq, var_shape.d, lens)
+        t = ms["varlen"] / 1e3
+        at_peak += flops / PEAK_BF16_FLOPS
+        parts["varlen"] = {"ms": round(ms["varlen"], 4), "ms_min": round(min(per["varlen"]), 4),
+                           "tflops": round(flops / t / 1e12, 1), "frac_of_peak": round(flops / t / PEAK_BF16_FLOPS, 4),
+                           "flops_per_launch": flops}
     if app_shape is not None:
         nbytes = app_in.algorithmic_bytes()
         t = ms["append"] / 1e3
@@ -342,9 +388,10 @@ def main():
 
     # Dominant kernel's roofline (the one with the larger share of the step).
     dom = max(names, key=lambda n: ms[n])
-    if dom in ("prefill", "chunk"):
+    if dom in ("prefill", "chunk", "varlen"):
         src = kernel_source_hash(["prefill_bf16.hip", "device_common.h"])
-        roof = {"kernel": "prefill_bf16_kernel" + (" (paged form)" if dom == "chunk" else ""), "bound": "mfma",
+        form = {"prefill": "", "chunk": " (paged form)", "varlen": " (packed form)"}[dom]
+        roof = {"kernel": "prefill_bf16_kernel" + form, "bound": "mfma",
                 "achieved": parts[dom]["tflops"], "peak": PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s",
                 "frac": round(parts[dom]["tflops"] * 1e12 / PEAK_BF16_FLOPS, 4),
                 "traffic": measured_traffic(args.workload, "prefill_bf16_kernel", src), "source_hash": src}
@@ -368,6 +415,9 @@ def main():
     if dec_inputs is not None:
         cfg["seed_decode"] = 100 + args.workload
         cfg["decode_tokens"] = int(dec_inputs.seq_lens.sum())
+    if var_in is not None:
+        cfg["seed_varlen"] = args.workload
+        cfg["varlen_lens"] = (var_in[3][1:] - var_in[3][:-1]).tolist()
     if app_in is not None:
         cfg["seed_append"] = args.workload
         cfg["append_seq_lens"] = app_in.seq_lens.tolist()
@@ -392,6 +442,8 @@ def main():
         result["cpu_baseline"] = cpu_baseline_chunk(chunk_in)
     if not args.no_cpu_baseline and args.workload == 7:
         result["cpu_baseline"] = cpu_baseline_append(app_in)
+    if not args.no_cpu_baseline and args.workload == 8:
+        result["cpu_baseline"] = cpu_baseline_varlen(var_in, var_shape)
     print(json.dumps(result), flush=True)
 
 
