@@ -286,3 +286,33 @@ def prefill_varlen(q, k, v, cu_seqlens, scale):
             o, l = _attend(q[first:last, h], k[first:last, g], v[first:last, g], float(scale), seen)
             out[first:last, h], lse[first:last, h] = o, l
     return out, lse
+
+
+def fp8_e4m3_value(codes):
+    """Real value of FP8 E4M3 codes (the OCP 8-bit float, finite-only form).
+
+    Bit 7 is the sign, bits 6..3 the exponent (bias 7), bits 2..0 the
+    mantissa.  Exponent 0 holds subnormals m/8 * 2^-6; codes with all
+    exponent and mantissa bits set (0x7F, 0xFF) are NaN; there is no
+    infinity, so the largest finite magnitude is 1.75 * 2^8 = 448.
+    """
+    c = np.asarray(codes, dtype=np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * 2.0 ** (e - 7))
+    return np.where((c & 0x7F) == 0x7F, np.nan, sign * mag)
+
+
+def decode_paged_fp8(q, k_codes, v_codes, k_scale, v_scale, block_table, seq_lens, scale, page_size):
+    """Single-token decode over a paged cache whose keys and values are FP8 E4M3.
+
+    The cache stores codes [num_pages, Hkv, page_size, d] with one scale per
+    tensor: key = fp8_e4m3_value(code) * k_scale, likewise for values (the
+    FP8 KV cache of the microLLM-rocm README, "Why this project exists", on
+    MI300X; gfx950's FP8 formats).  The result is decode_paged over those
+    real values.
+    """
+    keys = fp8_e4m3_value(k_codes) * float(k_scale)
+    vals = fp8_e4m3_value(v_codes) * float(v_scale)
+    return decode_paged(q, keys, vals, block_table, seq_lens, scale, page_size)

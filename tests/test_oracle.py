@@ -481,6 +481,41 @@ def test_varlen_brute_force():
                 assert abs(lse[t, h] - l) < 1e-13
 
 
+# ---------------------------------------------------------------- FP8 E4M3 KV cache
+def test_fp8_codes_match_torch():
+    """All 256 codes against torch's float8_e4m3fn (an independent implementation of the format)."""
+    want = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).double().numpy()
+    got = oracle.fp8_e4m3_value(np.arange(256))
+    np.testing.assert_array_equal(np.isnan(got), np.isnan(want))
+    np.testing.assert_array_equal(got[~np.isnan(got)], want[~np.isnan(want)])
+
+
+def test_fp8_known_codes():
+    cases = {0x38: 1.0, 0xB8: -1.0, 0x7E: 448.0, 0x01: 2.0 ** -9, 0x08: 2.0 ** -6, 0x07: 7 * 2.0 ** -9, 0x40: 2.0,
+             0x00: 0.0, 0x5C: 24.0}
+    for code, val in cases.items():
+        assert oracle.fp8_e4m3_value(code) == val, hex(code)
+    assert np.isnan(oracle.fp8_e4m3_value(0x7F)) and np.isnan(oracle.fp8_e4m3_value(0xFF))
+
+
+def test_fp8_decode_equals_decode_of_exact_values():
+    """K/V values that FP8 holds exactly (n/4, |n| <= 7): the FP8 decode with scales equals the
+    plain decode of the scaled values; distinct scales tell K from V."""
+    r = rng(60)
+    Hq, Hkv, d, ps = 4, 2, 6, 4
+    L = np.array([5, 12])
+    P = 5
+    table = np.array([[3, 0, -1], [1, 4, 2]])
+    kn = r.integers(-7, 8, size=(P, Hkv, ps, d)) / 4.0
+    vn = r.integers(-7, 8, size=(P, Hkv, ps, d)) / 4.0
+    to_code = lambda x: torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    q = r.standard_normal((2, Hq, d))
+    out, lse = oracle.decode_paged_fp8(q, to_code(kn), to_code(vn), 0.75, 3.0, table, L, 0.6, ps)
+    ref_o, ref_l = oracle.decode_paged(q, kn * 0.75, vn * 3.0, table, L, 0.6, ps)
+    np.testing.assert_allclose(out, ref_o, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(lse, ref_l, rtol=0, atol=1e-13)
+
+
 # ---------------------------------------------------------------- golden closed forms
 def _read_fixture(name):
     header, rows, cols = {}, [], None

@@ -66,6 +66,11 @@ MUTATIONS = {
                                           "_attend(q[first:last, h], k[:n, g], v[:n, g]")],
     "varlen mask not causal": [("seen = np.tril(np.ones((n, n), dtype=bool))", "seen = np.ones((n, n), dtype=bool)")],
     "varlen heads taken modulo": [("g = kv_head_of(h, Hq, Hkv)", "g = h % Hkv")],
+    "fp8 exponent bias 8": [("(1.0 + m / 8.0) * 2.0 ** (e - 7)", "(1.0 + m / 8.0) * 2.0 ** (e - 8)")],
+    "fp8 subnormals without the 2^-6": [("m / 8.0 * 2.0 ** -6", "m / 8.0 * 2.0 ** -7")],
+    "fp8 sign ignored": [("sign = np.where(c & 0x80, -1.0, 1.0)", "sign = 1.0")],
+    "fp8 value scale on the keys": [("vals = fp8_e4m3_value(v_codes) * float(v_scale)",
+                                     "vals = fp8_e4m3_value(v_codes) * float(k_scale)")],
     "append writes V into K": [("k_out[page, :, position % page_size] = np.asarray(k_new)[b, :, t]",
                                 "k_out[page, :, position % page_size] = np.asarray(v_new)[b, :, t]")],
 }
