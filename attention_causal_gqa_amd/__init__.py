@@ -1,5 +1,5 @@
 """Causal MHA/GQA attention for MI355X (gfx950): bf16 MFMA prefill (dense, ragged over packed tokens, or
-chunked over a paged cache), paged split-KV decode, and the paged-cache KV append.
+chunked over a paged cache), paged split-KV decode (bf16 or FP8 E4M3 cache), and the paged-cache KV append.
 
 The compute lives in ``libattn.so`` (hand-written HIP kernels behind the C ABI
 declared in ``include/attn.h``); this package is its ctypes binding, with the
@@ -19,6 +19,7 @@ from ._binding import (  # noqa: F401
     AttnError,
     attn_decode_num_splits,
     attn_decode_paged,
+    attn_decode_paged_fp8,
     attn_decode_workspace_bytes,
     attn_kv_append,
     attn_last_error_message,

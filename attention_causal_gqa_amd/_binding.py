@@ -61,6 +61,9 @@ def load_library():
     lib.attn_kv_append.restype = i32
     lib.attn_validate_chunk_metadata.argtypes = [vp, vp, i32, i32, i32, i32, i32]
     lib.attn_validate_chunk_metadata.restype = i32
+    lib.attn_decode_paged_fp8.argtypes = [vp, vp, vp, f32, f32, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
+                                          f32, i32, vp, sz, vp]
+    lib.attn_decode_paged_fp8.restype = i32
     lib.attn_validate_paged_metadata.argtypes = [vp, vp, i32, i32, i32, i32]
     lib.attn_validate_paged_metadata.restype = i32
     lib.attn_status_string.argtypes = [i32]
@@ -278,6 +281,50 @@ def attn_decode_paged(q, k_pages, v_pages, block_table, seq_lens, out=None, lse=
     _check(lib.attn_decode_paged(_ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table), _ptr(seq_lens), _ptr(out),
                                  None if lse is False else _ptr(lse), B, Hq, Hkv, d, page_size, P, W, float(scale),
                                  _dtype_code(q), num_splits, _ptr(workspace), ws_bytes, _stream(stream)))
+    return out, (None if lse is False else lse)
+
+
+def attn_decode_paged_fp8(q, k_pages, v_pages, k_scale, v_scale, block_table, seq_lens, out=None, lse=None,
+                          scale=None, num_splits=0, workspace=None, stream=None):
+    """Paged single-token decode over an FP8 E4M3 cache.  q [B,Hq,d] bf16; pools [P,Hkv,page,d] uint8 codes
+    (or torch.float8_e4m3fn); key = code value * k_scale, value = code value * v_scale."""
+    torch = _torch()
+    _require(q.dim() == 3 and k_pages.dim() == 4 and k_pages.shape == v_pages.shape, "bad q / page pool shapes")
+    B, Hq, d = q.shape
+    P, Hkv, page_size, dk = k_pages.shape
+    _require(dk == d, "page pools and q disagree on d")
+    fp8 = getattr(torch, "float8_e4m3fn", None)
+    _require(k_pages.dtype in (torch.uint8, fp8) and v_pages.dtype in (torch.uint8, fp8),
+             "FP8 pools must be uint8 codes or float8_e4m3fn")
+    _require(q.dtype == torch.bfloat16, "q must be bfloat16")
+    _require(block_table.dim() == 2 and block_table.shape[0] == B and block_table.dtype == torch.int32,
+             "block_table must be int32 [B, W]")
+    _require(seq_lens.shape == (B,) and seq_lens.dtype == torch.int32, "seq_lens must be int32 [B]")
+    for n, t in (("q", q), ("k_pages", k_pages), ("v_pages", v_pages), ("block_table", block_table),
+                 ("seq_lens", seq_lens)):
+        _dense_on_gpu(n, t)
+    W = block_table.shape[1]
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    _dense_on_gpu("out", out)
+    _require(out.shape == q.shape and out.dtype == q.dtype, "out must match q")
+    if lse is not False:
+        _dense_on_gpu("lse", lse)
+        _require(lse.shape == (B, Hq) and lse.dtype == torch.float32, "lse must be float32 [B, Hq]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    lib = load_library()
+    need = lib.attn_decode_workspace_bytes(B, Hq, Hkv, d, page_size, W, num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _dense_on_gpu("workspace", workspace)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib.attn_decode_paged_fp8(_ptr(q), _ptr(k_pages), _ptr(v_pages), float(k_scale), float(v_scale),
+                                     _ptr(block_table), _ptr(seq_lens), _ptr(out), None if lse is False else _ptr(lse),
+                                     B, Hq, Hkv, d, page_size, P, W, float(scale), num_splits, _ptr(workspace),
+                                     ws_bytes, _stream(stream)))
     return out, (None if lse is False else lse)
 
 

@@ -310,6 +310,39 @@ int attn_decode_paged(const void* q, const void* k_pages, const void* v_pages, c
     return from_hip(attn::launch_decode_bf16(a, stream), "attn_decode_paged launch");
 }
 
+int attn_decode_paged_fp8(const void* q, const void* k_pages, const void* v_pages, float k_scale, float v_scale,
+                          const int32_t* block_table, const int32_t* seq_lens, void* out, float* lse, int B, int Hq,
+                          int Hkv, int d, int page_size, int num_pages, int max_pages_per_seq, float scale,
+                          int num_splits, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    g_last_error.clear();
+    int st = check_decode_sizes(B, Hq, Hkv, d, page_size, max_pages_per_seq, num_splits);
+    if (st != ATTN_OK) return st;
+    if (num_pages < 0) return fail(ATTN_ERR_INVALID_ARG, "num_pages=%d must be >= 0", num_pages);
+    if (!std::isfinite(scale)) return fail(ATTN_ERR_INVALID_ARG, "scale must be finite");
+    if (!std::isfinite(k_scale) || !std::isfinite(v_scale))
+        return fail(ATTN_ERR_INVALID_ARG, "k_scale and v_scale must be finite");
+    if (B == 0) return ATTN_OK;
+    if (!q || !k_pages || !v_pages || !block_table || !seq_lens || !out)
+        return fail(ATTN_ERR_INVALID_ARG, "q, k_pages, v_pages, block_table, seq_lens and out must be non-null");
+    if (!aligned(q, 16) || !aligned(k_pages, 16) || !aligned(v_pages, 16) || !aligned(out, 16))
+        return fail(ATTN_ERR_INVALID_ARG, "q, k_pages, v_pages and out must be 16-byte aligned");
+    if (!aligned(block_table, 4) || !aligned(seq_lens, 4) || (lse && !aligned(lse, 4)))
+        return fail(ATTN_ERR_INVALID_ARG, "block_table, seq_lens and lse must be 4-byte aligned");
+    const Plan plan = make_plan(B, Hkv, max_pages_per_seq, num_splits);
+    if ((int64_t)B * Hq > kMaxGrid) return fail(ATTN_ERR_INVALID_ARG, "problem too large");
+    const size_t need = workspace_for(B, Hq, d, plan);
+    if (!workspace || workspace_bytes < need)
+        return fail(ATTN_ERR_WORKSPACE, "workspace %zu bytes given, %zu needed", workspace ? workspace_bytes : 0, need);
+    if (!aligned(workspace, 16)) return fail(ATTN_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+    const size_t n = (size_t)B * Hq * plan.splits;
+    float* o_part = static_cast<float*>(workspace);
+    float* lse_part = reinterpret_cast<float*>(static_cast<char*>(workspace) + round256(n * d * sizeof(float)));
+    attn::DecodeArgs a{q,      k_pages,  v_pages, block_table, seq_lens, out, lse, o_part, lse_part, B,
+                       Hq,     Hkv,      d,       page_size,   max_pages_per_seq, plan.splits,
+                       plan.pages_per_split, scale};
+    return from_hip(attn::launch_decode_fp8(a, k_scale, v_scale, stream), "attn_decode_paged_fp8 launch");
+}
+
 int attn_validate_chunk_metadata(const int32_t* block_table_host, const int32_t* seq_lens_host, int B,
                                  int max_pages_per_seq, int page_size, int num_pages, int chunk_len) {
     g_last_error.clear();

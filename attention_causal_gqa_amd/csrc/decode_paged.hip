@@ -17,11 +17,21 @@
 // output and log-sum-exp go to the workspace slot of the piece's first item
 // (a fixed run of pages_per_split pages).
 //
+// FP8 form (kFp8): the pools hold FP8 E4M3 codes with one scale per tensor
+// (the FP8 KV cache of the microLLM-rocm README, "Why this project exists";
+// gfx950's OCP FP8 formats).  A page slice is half as many bytes; K arrives
+// 8 bytes per lane and is widened to bf16 in registers
+// (v_cvt_scalef32_pk_bf16_fp8, exact: every E4M3 value is a bf16 value),
+// V is DMA'd to LDS as FP8 and widened into the bf16 slice layout the
+// transposing reads use.  The key scale is folded into the score factor,
+// the value scale into the normalisation at the flush.
+//
 // Combine kernel: per (sequence, query head), the pieces' partial results are
 // merged with log-sum-exp weights (block-wise softmax statistics,
 // llm-from-scratch "Project Overview", "Performance Layer: kernel/ and
 // parallel/").
 #include <atomic>
+#include <type_traits>
 
 #include "device_common.h"
 #include "kernels.h"
@@ -60,6 +70,18 @@ __device__ __forceinline__ u32x4 gload16(const void* p) {
     u32x4 r;
     asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(r) : "v"(p) : "memory");
     return r;
+}
+__device__ __forceinline__ u32x2 gload8(const void* p) {
+    u32x2 r;
+    asm volatile("global_load_dwordx2 %0, %1, off" : "=v"(r) : "v"(p) : "memory");
+    return r;
+}
+// Four FP8 E4M3 codes -> four bf16 (exact), as two packed dwords.
+__device__ __forceinline__ u32x2 fp8x4_to_bf16(uint32_t c) {
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    const bf16x2_t lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c, 1.0f, false);
+    const bf16x2_t hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c, 1.0f, true);
+    return u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
 }
 // 16 bytes per lane, HBM -> LDS: lane l's bytes land at lds + 16 l (lds is
 // wave-uniform, passed in M0).
@@ -131,24 +153,29 @@ __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
 //                  comes HBM -> LDS by DMA and is read transposed)
 // The next page's K and V loads are in flight while a page is computed, and
 // the block-table entry of the page after that is loaded a step earlier.
-template <int D>
-__global__ __launch_bounds__(64) void decode_stream_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kp,
-                                                            const bf16* __restrict__ vp,
+template <int D, bool kFp8>
+__global__ __launch_bounds__(64) void decode_stream_kernel(const bf16* __restrict__ q, const char* __restrict__ kp,
+                                                            const char* __restrict__ vp,
                                                             const int32_t* __restrict__ block_table,
                                                             const int32_t* __restrict__ seq_lens,
                                                             float* __restrict__ o_part, float* __restrict__ lse_part,
                                                             int B, int Hq, int Hkv, int G, int W, int S, int pps,
-                                                            float c1) {
+                                                            float c1, float vscale) {
     constexpr int NKK = D / 32;        // k-steps of QK^T (16x16x32)
     constexpr int NB = D / 16;         // 16-column blocks of O (16x16x16)
-    constexpr int ROWB = D * 2;        // bytes per token row
-    constexpr int SLICEB = kPage * ROWB;  // bytes per (page, kv head) slice
-    constexpr int NDMA = SLICEB / 1024;   // wave-wide 1 KiB DMAs per slice
-    constexpr int RPD = 1024 / ROWB;      // rows per DMA
-    constexpr int CPR = D / 8;            // 16-byte chunks per row
-    // Two V slices (double buffer).
-    __shared__ __attribute__((aligned(1024))) char Vb0[SLICEB];
-    __shared__ __attribute__((aligned(1024))) char Vb1[SLICEB];
+    constexpr int ROWB = D * 2;        // bytes per token row in bf16 (the LDS layout of V)
+    constexpr int SLICEB = kPage * ROWB;  // bytes per bf16 (page, kv head) slice
+    constexpr int CPR = D / 8;            // 16-byte bf16 chunks per row
+    constexpr int KROWB = kFp8 ? D : ROWB;           // bytes per token row in the pools
+    constexpr int KSLICEB = kPage * KROWB;           // bytes per pool slice
+    constexpr int NDMA = KSLICEB / 1024;             // wave-wide 1 KiB DMAs per slice
+    constexpr int RPD = 1024 / KROWB;                // rows per DMA
+    constexpr int KCPR = KROWB / 16;                 // 16-byte chunks per pool row
+    // Two slices of V as it arrives (double buffer); the FP8 form widens the
+    // current one into Vw, read by the PV MFMAs.
+    __shared__ __attribute__((aligned(1024))) char Vb0[KSLICEB];
+    __shared__ __attribute__((aligned(1024))) char Vb1[KSLICEB];
+    __shared__ __attribute__((aligned(1024))) char Vw[kFp8 ? SLICEB : 16];
 
     const int lane = threadIdx.x;
     const int hd = lane & 15;  // head column (S^T, P) / d within a 16-block (O)
@@ -246,6 +273,7 @@ __global__ __launch_bounds__(64) void decode_stream_kernel(const bf16* __restric
     // Q^T as the B operand of S^T: lane holds Q[head hd][32kk + 8g .. +7].
     // Columns hd >= G repeat head G - 1; their results are never stored.
     bf16x8 qb[NKK];
+    typedef std::conditional_t<kFp8, u32x2, u32x4> KReg;  // a lane's K A-operand as it arrives
     auto load_q = [&](int b, int kvh) __attribute__((always_inline)) {
         const int hh = hd < G ? hd : G - 1;
         const bf16* qrow = q + ((size_t)b * Hq + (size_t)kvh * G + hh) * D + 8 * g;
@@ -254,14 +282,16 @@ __global__ __launch_bounds__(64) void decode_stream_kernel(const bf16* __restric
     };
 
     // K A-operand: lane holds K[token hd][32kk + 8g .. +7].
-    const uint32_t koff = (uint32_t)(hd * ROWB + 16 * g);
-    // V DMA: DMA n fills slice bytes [1024n, +1024) = rows RPD*n + lane/CPR,
-    // position lane % CPR, i.e. logical chunk (lane % CPR) ^ vswz(row).
+    const uint32_t koff = (uint32_t)(hd * KROWB + (kFp8 ? 8 : 16) * g);
+    // V DMA: DMA n fills slice bytes [1024n, +1024) = rows RPD*n + lane/KCPR,
+    // position lane % KCPR.  bf16: logical chunk (lane % CPR) ^ vswz(row),
+    // the swizzled layout the transposing reads expect; FP8: in order (the
+    // widening pass swizzles).
     uint32_t voff[NDMA];
 #pragma unroll
     for (int n = 0; n < NDMA; ++n) {
-        const int row = RPD * n + lane / CPR;
-        voff[n] = (uint32_t)(row * ROWB + 16 * ((lane % CPR) ^ vswz<D>(row)));
+        const int row = RPD * n + lane / KCPR;
+        voff[n] = (uint32_t)(row * KROWB + 16 * (kFp8 ? lane % KCPR : (lane % CPR) ^ vswz<D>(row)));
     }
     // V B-operand (transposing read): lane i of 16-lane row g points at token
     // row 4g + i/4, columns 16nb + 4(i%4); chunk 2nb + (i%4)/2 of that row.
@@ -269,12 +299,15 @@ __global__ __launch_bounds__(64) void decode_stream_kernel(const bf16* __restric
     const int vrow = 4 * g + (vi >> 2);
     const int vread = vrow * ROWB + 8 * (vi & 1) + ((((vi & 3) >> 1) ^ vswz<D>(vrow)) << 4);
 
-    auto issue_page = [&](int pid, int kvh, char* vdst, u32x4(&ka)[NKK]) __attribute__((always_inline)) {
-        const size_t slice = ((size_t)pid * Hkv + kvh) * (kPage * D);
-        const char* kb = reinterpret_cast<const char*>(kp + slice);
+    auto issue_page = [&](int pid, int kvh, char* vdst, KReg(&ka)[NKK]) __attribute__((always_inline)) {
+        const size_t slice = ((size_t)pid * Hkv + kvh) * KSLICEB;
+        const char* kb = kp + slice;
 #pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) ka[kk] = gload16(kb + koff + 64 * kk);
-        const char* vb = reinterpret_cast<const char*>(vp + slice);
+        for (int kk = 0; kk < NKK; ++kk) {
+            if constexpr (kFp8) ka[kk] = gload8(kb + koff + 32 * kk);
+            else ka[kk] = gload16(kb + koff + 64 * kk);
+        }
+        const char* vb = vp + slice;
 #pragma unroll
         for (int n = 0; n < NDMA; ++n) dma16(vb + voff[n], vdst + 1024 * n);
     };
@@ -290,11 +323,30 @@ __global__ __launch_bounds__(64) void decode_stream_kernel(const bf16* __restric
     };
     constexpr uint32_t kOnes = 0x3F803F80u;
 
-    auto compute_page = [&](const Cursor& c, const u32x4(&kcur)[NKK], char* vbuf) __attribute__((always_inline)) {
-        // Tokens past L in the last page: zero their V rows (the pool may
-        // hold NaN there, and 0 * NaN would reach O).
+    auto compute_page = [&](const Cursor& c, const KReg(&kcur)[NKK], char* vslot) __attribute__((always_inline)) {
         const int nvalid = c.L - c.j * kPage;
-        if (nvalid < kPage) {
+        char* vbuf = vslot;
+        if constexpr (kFp8) {
+            // Widen V into the bf16 layout: (row r, 8-value chunk cc) for
+            // chunk index lane + 64 i; rows past L become zeros (the pool may
+            // hold NaN codes there, and 0 * NaN would reach O).
+            constexpr int NCH = kPage * CPR / 64;
+#pragma unroll
+            for (int i = 0; i < NCH; ++i) {
+                const int n = lane + 64 * i;
+                const int r = n / CPR, cc = n % CPR;
+                u32x4 wv = {0u, 0u, 0u, 0u};
+                if (r < nvalid) {
+                    const u32x2 f = *reinterpret_cast<const u32x2*>(vslot + r * KROWB + 8 * cc);
+                    const u32x2 a = fp8x4_to_bf16(f.x), b2 = fp8x4_to_bf16(f.y);
+                    wv = u32x4{a.x, a.y, b2.x, b2.y};
+                }
+                *reinterpret_cast<u32x4*>(Vw + r * ROWB + 16 * (cc ^ vswz<D>(r))) = wv;
+            }
+            vbuf = Vw;
+        } else if (nvalid < kPage) {
+            // Tokens past L in the last page: zero their V rows (the pool may
+            // hold NaN there, and 0 * NaN would reach O).
 #pragma unroll
             for (int n = 0; n < NDMA; ++n) {
                 const int row = RPD * n + lane / CPR;
@@ -304,8 +356,16 @@ __global__ __launch_bounds__(64) void decode_stream_kernel(const bf16* __restric
         }
         f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kk = 0; kk < NKK; ++kk)
-            sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kcur[kk]), qb[kk], sacc, 0, 0, 0);
+        for (int kk = 0; kk < NKK; ++kk) {
+            u32x4 kop;
+            if constexpr (kFp8) {
+                const u32x2 a = fp8x4_to_bf16(kcur[kk].x), b2 = fp8x4_to_bf16(kcur[kk].y);
+                kop = u32x4{a.x, a.y, b2.x, b2.y};
+            } else {
+                kop = kcur[kk];
+            }
+            sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kop), qb[kk], sacc, 0, 0, 0);
+        }
         // lane holds S^T[token 4g + i][head hd]
         float x[4];
 #pragma unroll
@@ -354,7 +414,7 @@ __global__ __launch_bounds__(64) void decode_stream_kernel(const bf16* __restric
         // Row sums: add the four 16-lane rows (tokens 4g..4g+3).
         const float lr = pair_sum(row_pair_sum(l_run));
         const float ll = pair_sum(row_pair_sum(l_lse));
-        const float inv = 1.f / lr;
+        const float inv = vscale / lr;
         const size_t bh0 = (size_t)pb * Hq + (size_t)pkvh * G;
         // lane holds O[head 4g + i][16nb + hd]
 #pragma unroll
@@ -374,13 +434,13 @@ __global__ __launch_bounds__(64) void decode_stream_kernel(const bf16* __restric
     // next page's loads go into the other set while this page is computed.
     // The V buffers are distinct arrays, so the compiler does not make LDS
     // reads wait for the other buffer's DMA.
-    u32x4 ka0[NKK], ka1[NKK];
+    KReg ka0[NKK], ka1[NKK];
     issue_page(page_id(cc), cc.kvh, Vb0, ka0);
     Cursor cf = cc;  // page whose loads go out next
     advance(cf);
     int pid_f = cf.x < xe ? page_id(cf) : 0;
 
-    auto step = [&](u32x4(&kx)[NKK], char* bx, u32x4(&ky)[NKK], char* by) __attribute__((always_inline)) {
+    auto step = [&](KReg(&kx)[NKK], char* bx, KReg(&ky)[NKK], char* by) __attribute__((always_inline)) {
         const bool first_of_run = cc.j == 0 || cc.x == xs;
         if (first_of_run) load_q(cc.b, cc.kvh);
         const bool more = cf.x < xe;
@@ -515,7 +575,7 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(const float* __restr
 
 // Workgroups of the streaming kernel that are resident at once on the
 // current device (compute units x occupancy), found once per device.
-template <int D>
+template <int D, bool kFp8>
 hipError_t stream_waves(int* nw) {
     static std::atomic<int> cache[kMaxDevices];
     int dev = 0;
@@ -526,7 +586,8 @@ hipError_t stream_waves(int* nw) {
     if (v == 0) {
         int cus = 0, per = 0;
         if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
-        if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, decode_stream_kernel<D>, 64, 0)) != hipSuccess)
+        if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, decode_stream_kernel<D, kFp8>, 64, 0)) !=
+            hipSuccess)
             return e;
         v = cus * (per > 0 ? per : 1);
         cache[dev].store(v, std::memory_order_relaxed);
@@ -535,22 +596,22 @@ hipError_t stream_waves(int* nw) {
     return hipSuccess;
 }
 
-template <int D>
-hipError_t launch_split(const DecodeArgs& a, hipStream_t stream, float c1) {
+template <int D, bool kFp8>
+hipError_t launch_split(const DecodeArgs& a, hipStream_t stream, float c1, float vscale) {
     int nw = 0;
-    const hipError_t e = stream_waves<D>(&nw);
+    const hipError_t e = stream_waves<D, kFp8>(&nw);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((decode_stream_kernel<D>), dim3((unsigned)nw), dim3(64), 0, stream, (const bf16*)a.q,
-                       (const bf16*)a.k_pages, (const bf16*)a.v_pages, a.block_table, a.seq_lens, a.o_part, a.lse_part,
-                       a.B, a.Hq, a.Hkv, a.Hq / a.Hkv, a.W, a.num_splits, a.pages_per_split, c1);
+    hipLaunchKernelGGL((decode_stream_kernel<D, kFp8>), dim3((unsigned)nw), dim3(64), 0, stream, (const bf16*)a.q,
+                       (const char*)a.k_pages, (const char*)a.v_pages, a.block_table, a.seq_lens, a.o_part,
+                       a.lse_part, a.B, a.Hq, a.Hkv, a.Hq / a.Hkv, a.W, a.num_splits, a.pages_per_split, c1, vscale);
     return hipGetLastError();
 }
 
-}  // namespace
-
-hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream) {
-    const float c1 = (float)((double)a.scale * 1.4426950408889634);
-    const hipError_t e = a.d == 128 ? launch_split<128>(a, stream, c1) : launch_split<64>(a, stream, c1);
+template <bool kFp8>
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream, float kscale, float vscale) {
+    const float c1 = (float)((double)a.scale * (double)kscale * 1.4426950408889634);
+    const hipError_t e = a.d == 128 ? launch_split<128, kFp8>(a, stream, c1, vscale)
+                                    : launch_split<64, kFp8>(a, stream, c1, vscale);
     if (e != hipSuccess) return e;
     if (a.d == 128) {
         hipLaunchKernelGGL(decode_combine_kernel<128>, dim3((unsigned)a.B * a.Hq), dim3(64), 0, stream, a.o_part,
@@ -560,6 +621,16 @@ hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream) {
                            a.lse_part, a.seq_lens, (bf16*)a.out, a.lse, a.Hq, a.num_splits, a.pages_per_split);
     }
     return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream) {
+    return launch_decode<false>(a, stream, 1.0f, 1.0f);
+}
+
+hipError_t launch_decode_fp8(const DecodeArgs& a, float kscale, float vscale, hipStream_t stream) {
+    return launch_decode<true>(a, stream, kscale, vscale);
 }
 
 }  // namespace attn

@@ -54,6 +54,8 @@ hipError_t launch_prefill_paged_bf16(const PrefillArgs& a, const int32_t* block_
 // longest sequence.
 hipError_t launch_prefill_varlen_bf16(const PrefillArgs& a, const int32_t* cu_seqlens, hipStream_t stream);
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream);
+// FP8 E4M3 page pools (one byte per value) with per-tensor scales.
+hipError_t launch_decode_fp8(const DecodeArgs& a, float kscale, float vscale, hipStream_t stream);
 hipError_t launch_kv_append_bf16(const KvAppendArgs& a, hipStream_t stream);
 
 }  // namespace attn

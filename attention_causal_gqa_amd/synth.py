@@ -133,6 +133,9 @@ WORKLOADS[7] = {"append": ChunkShape(4, 32, 8, 2048, 128, PAGE_SIZE, 4096, 16384
 # Ragged prefill (seed 8): 16 sequences of 256..4096 tokens packed along the token axis.
 WORKLOADS[8] = {"varlen": VarlenShape(16, 32, 8, 128, 256, 4096, torch.bfloat16)}
 
+# Paged decode over an FP8 E4M3 cache (seed 109): workload 5's decode shape.
+WORKLOADS[9] = {"decode_fp8": DecodeShape(64, 32, 8, 128, PAGE_SIZE, 1024, 8192, torch.bfloat16)}
+
 WORKLOAD_NAMES = {
     1: "causal MHA prefill fp32 B1 H4 T128 d64",
     2: "causal GQA prefill bf16 B1 Hq16 Hkv8 T512 d128",
@@ -142,6 +145,7 @@ WORKLOAD_NAMES = {
     6: "chunked prefill bf16 over a paged cache B4 Hq32 Hkv8 Tq2048 d128 page16 L~U[4096,16384]",
     7: "KV append bf16 into a paged cache B4 Hkv8 Tn2048 d128 page16 L~U[4096,16384]",
     8: "ragged prefill bf16 over packed tokens S16 Hq32 Hkv8 d128 T~U[256,4096]",
+    9: "paged decode over an FP8 E4M3 cache B64 Hq32 Hkv8 d128 page16 L~U[1024,8192]",
 }
 
 
@@ -298,6 +302,50 @@ def append_inputs(shape: ChunkShape, seed: int, *, seq_lens=None, poison=None):
     k_new = torch.randn(B, shape.Hkv, shape.Tq, shape.d, generator=g).to(shape.dtype)
     v_new = torch.randn(B, shape.Hkv, shape.Tq, shape.d, generator=g).to(shape.dtype)
     return AppendInputs(k_new, v_new, k_pages, v_pages, table, seq_lens.to(torch.int32), shape.page_size)
+
+
+@dataclass
+class Fp8PagedInputs:
+    q: torch.Tensor            # [B, Hq, d] bf16
+    k_codes: torch.Tensor      # [num_pages, Hkv, page_size, d] uint8, FP8 E4M3 codes
+    v_codes: torch.Tensor
+    k_scale: float
+    v_scale: float
+    block_table: torch.Tensor  # [B, W] int32
+    seq_lens: torch.Tensor     # [B] int32
+    page_size: int
+
+    def algorithmic_bytes(self) -> int:
+        """K/V codes of valid tokens (one byte each) + q + out + used block-table entries + seq_lens."""
+        Hkv, d = self.k_codes.shape[1], self.k_codes.shape[3]
+        used = int(((self.seq_lens.long() + self.page_size - 1) // self.page_size).sum())
+        return 2 * int(self.seq_lens.sum()) * Hkv * d + 2 * self.q.numel() * 2 + 4 * used + 4 * self.seq_lens.numel()
+
+
+def fp8_paged_inputs(shape: DecodeShape, seed: int, *, seq_lens=None, poison_nan=False):
+    """Paged decode inputs quantised to FP8 E4M3: draw as paged_inputs (seq_lens, permutation, q, K, V in
+    float32), then scale each pool by 448 / max|x| and round to the nearest E4M3 code (torch's float8_e4m3fn
+    cast); k_scale / v_scale are the inverse factors, so code value * scale approximates the drawn value.
+    ``poison_nan`` writes the NaN code 0x7F into every slot no valid token occupies."""
+    g = torch.Generator().manual_seed(seed)
+    B = shape.B
+    if seq_lens is None:
+        seq_lens = torch.randint(shape.L_lo, shape.L_hi + 1, (B,), generator=g)
+    seq_lens = torch.as_tensor(seq_lens, dtype=torch.int64)
+    table, num_pages = _pool_layout(seq_lens, shape.page_size, shape.max_pages_per_seq, g, 0)
+    q = torch.randn(B, shape.Hq, shape.d, generator=g).to(torch.bfloat16)
+    pool_shape = (num_pages, shape.Hkv, shape.page_size, shape.d)
+    codes, scales = [], []
+    for _ in range(2):
+        x = torch.randn(pool_shape, generator=g)
+        s = float(x.abs().max()) / 448.0
+        c = (x / s).to(torch.float8_e4m3fn).view(torch.uint8).clone()
+        if poison_nan:
+            _poison(c, table, seq_lens, shape.page_size, 0, 0x7F)
+        codes.append(c)
+        scales.append(s)
+    return Fp8PagedInputs(q, codes[0], codes[1], scales[0], scales[1], table, seq_lens.to(torch.int32),
+                          shape.page_size)
 
 
 def paged_from_dense(k, v, seq_lens, page_size, seed, W=None, poison=None):

@@ -26,6 +26,10 @@
  *    of the sequence's cached keys, causally.  It is the prefill kernel
  *    reading its key/value tiles page by page through the block table.
  *
+ *  - attn_decode_paged_fp8: the same decode over a cache whose keys and
+ *    values are stored as FP8 E4M3 with one scale per tensor (the FP8 KV
+ *    cache of the microLLM-rocm README, "Why this project exists").
+ *
  *  - attn_prefill_varlen: causal prefill of a ragged batch, sequences of
  *    different lengths packed token after token (ragged / varlen prefill,
  *    RoseLLM README, "Systems highlights", "Inference and serving"); each
@@ -235,6 +239,29 @@ int attn_decode_paged(const void* q, const void* k_pages, const void* v_pages,
                       int max_pages_per_seq, float scale, attn_dtype_t dtype,
                       int num_splits, void* workspace, size_t workspace_bytes,
                       hipStream_t stream);
+
+/*
+ * Single-token decode over a paged KV cache stored in FP8 E4M3.
+ *
+ *   k_pages,v_pages: device, [num_pages, Hkv, page_size, d] bytes, each an
+ *                    FP8 E4M3 code (OCP 8-bit float: sign, 4-bit exponent with
+ *                    bias 7, 3-bit mantissa, subnormals, no infinity, 0x7F and
+ *                    0xFF NaN); the key at a slot is code value * k_scale, the
+ *                    value code value * v_scale
+ *   k_scale,v_scale: finite per-tensor scales
+ * Every other argument, the workspace and the result are as for
+ * attn_decode_paged (q, out, lse bf16 / fp32 as there; page_size = 16,
+ * d = 128 or 64, Hq / Hkv <= 16).  Codes at slots past seq_lens[b] may hold
+ * anything (NaN codes included); the cached codes of valid slots must not
+ * be NaN.
+ */
+int attn_decode_paged_fp8(const void* q, const void* k_pages, const void* v_pages,
+                          float k_scale, float v_scale,
+                          const int32_t* block_table, const int32_t* seq_lens,
+                          void* out, float* lse,
+                          int B, int Hq, int Hkv, int d, int page_size, int num_pages,
+                          int max_pages_per_seq, float scale, int num_splits,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Host-side check of paged metadata (host copies of block_table and

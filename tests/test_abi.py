@@ -28,7 +28,7 @@ def declared_functions():
 def test_header_declares_the_api():
     names = declared_functions()
     for n in ("attn_prefill", "attn_prefill_paged", "attn_prefill_varlen", "attn_validate_varlen_metadata",
-              "attn_kv_append", "attn_decode_paged", "attn_decode_workspace_bytes",
+              "attn_kv_append", "attn_decode_paged_fp8", "attn_decode_paged", "attn_decode_workspace_bytes",
               "attn_decode_num_splits", "attn_validate_paged_metadata", "attn_validate_chunk_metadata",
               "attn_status_string", "attn_last_error_message"):
         assert n in names
@@ -116,6 +116,32 @@ def decode(lib, q=FAKE, kp=FAKE, vp=FAKE, bt=FAKE, sl=FAKE, out=FAKE, lse=None, 
 )
 def test_decode_rejects(lib, kw, status):
     assert decode(lib, **kw) == status
+
+
+def decode_fp8(lib, q=FAKE, kp=FAKE, vp=FAKE, ks=1.0, vs=1.0, bt=FAKE, sl=FAKE, out=FAKE, B=2, Hq=4, Hkv=2, d=128,
+               ps=16, P=10, W=8, scale=0.1, ns=0, ws=FAKE, wsb=None):
+    if wsb is None:
+        wsb = lib.attn_decode_workspace_bytes(max(B, 0), Hq, Hkv, d, ps, W, ns) if B >= 0 else 0
+    return lib.attn_decode_paged_fp8(q, kp, vp, ks, vs, bt, sl, out, None, B, Hq, Hkv, d, ps, P, W, scale, ns, ws,
+                                     wsb, None)
+
+
+@pytest.mark.parametrize(
+    "kw,status",
+    [
+        (dict(kp=None), A.ATTN_ERR_INVALID_ARG),
+        (dict(vp=FAKE + 8), A.ATTN_ERR_INVALID_ARG),
+        (dict(ks=float("nan")), A.ATTN_ERR_INVALID_ARG),
+        (dict(vs=float("inf")), A.ATTN_ERR_INVALID_ARG),
+        (dict(Hq=6, Hkv=4), A.ATTN_ERR_INVALID_ARG),
+        (dict(W=0), A.ATTN_ERR_INVALID_ARG),
+        (dict(d=80), A.ATTN_ERR_UNSUPPORTED),
+        (dict(Hq=34, Hkv=2), A.ATTN_ERR_UNSUPPORTED),
+        (dict(ws=None), A.ATTN_ERR_WORKSPACE),
+    ],
+)
+def test_decode_fp8_rejects(lib, kw, status):
+    assert decode_fp8(lib, **kw) == status
 
 
 def test_decode_empty_batch_is_a_no_op(lib):
