@@ -16,13 +16,14 @@ GPU runs a short sleep kernel, so that the events time kernels rather than
 host launch latency.  A workload with a single part times its K queued
 launches between one pair of events instead (``ms_min`` stays per launch).
 
-    python bench.py [--steps K] [--warmup W] [--workload 5|3|4|6|7|8] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--workload 5|3|4|6|7|8|9] [--no-cpu-baseline]
 
 Workload 6 (not the default) times the chunked prefill over a paged cache:
 2048-token chunks at the end of four sequences of 4096..16384 cached tokens.
 Workload 7 times the KV append that writes such chunks into the cache.
 Workload 8 times the ragged prefill of 16 sequences of 256..4096 tokens
-packed along the token axis.
+packed along the token axis.  Workload 9 times the paged decode of workload
+5 over an FP8 E4M3 cache (algorithmic bytes: one byte per cached value).
     python bench.py --copy-calibration   # plain 1 GiB copy, reference for HBM byte counters
 """
 
@@ -54,7 +55,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workload", type=int, default=5, choices=(3, 4, 5, 6, 7, 8))
+    p.add_argument("--workload", type=int, default=5, choices=(3, 4, 5, 6, 7, 8, 9))
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--flush", action="store_true",
                    help="write a 512 MiB buffer before each step (outside the kernel events) to evict L2/MALL")
@@ -224,6 +225,32 @@ def cpu_baseline_varlen(var_in, shape, budget_s=20.0):
             "varlen_tflops": flops / t / 1e12, "host_cpu_count": os.cpu_count()}
 
 
+def cpu_baseline_fp8(inp, budget_s=20.0):
+    """Time the fp64 oracle's FP8 decode on a bounded sample: sequences one at a time."""
+    import oracle
+    from threadpoolctl import threadpool_info
+
+    threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    kc, vc = inp.k_codes.numpy(), inp.v_codes.numpy()
+    scale = synth.fp32_scale(inp.q.shape[2])
+    B, Hq, d = inp.q.shape
+    Hkv = kc.shape[1]
+    t0 = time.perf_counter()
+    seqs = nbytes = 0
+    while seqs < B and (seqs == 0 or time.perf_counter() - t0 < budget_s):
+        b = seqs
+        oracle.decode_paged_fp8(inp.q[b:b + 1].float().numpy(), kc, vc, inp.k_scale, inp.v_scale,
+                                inp.block_table[b:b + 1].numpy(), inp.seq_lens[b:b + 1].numpy(), scale, inp.page_size)
+        L = int(inp.seq_lens[b])
+        nbytes += 2 * L * Hkv * d + 2 * Hq * d * 2 + 4 * (-(-L // 16)) + 4
+        seqs += 1
+    t = time.perf_counter() - t0
+    return {"value": nbytes / t / PEAK_HBM_BYTES, "unit": "fraction of MI355X roofline", "cores": threads,
+            "kind": "oracle", "sample": f"fp64 oracle FP8 decode of {seqs} of {B} sequences ({t:.2f} s, pools "
+                                        f"decoded from codes inside each call)",
+            "decode_gbps": nbytes / t / 1e9, "host_cpu_count": os.cpu_count()}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -241,8 +268,9 @@ def main():
     chunk_shape = wl.get("chunk")
     app_shape = wl.get("append")
     var_shape = wl.get("varlen")
+    f8_shape = wl.get("decode_fp8")
 
-    pre_inputs = dec_inputs = chunk_in = app_in = var_in = None
+    pre_inputs = dec_inputs = chunk_in = app_in = var_in = f8_in = None
     work = {}
     if pre_shape is not None:
         pre_inputs = synth.prefill_inputs(pre_shape, seed=args.workload)
@@ -285,6 +313,18 @@ def main():
         vlse = torch.empty(vq.shape[:2], dtype=torch.float32, device=dev)
         vscale = synth.fp32_scale(var_shape.d)
         work["varlen"] = lambda: A.attn_prefill_varlen(vq, vk, vv, vcu, vT, out=vout, lse=vlse, scale=vscale)
+    if f8_shape is not None:
+        f8_in = synth.fp8_paged_inputs(f8_shape, seed=100 + args.workload)
+        fq, fkc, fvc, fbt, fsl = (t.to(dev) for t in (f8_in.q, f8_in.k_codes, f8_in.v_codes, f8_in.block_table,
+                                                      f8_in.seq_lens))
+        fout = torch.empty_like(fq)
+        flse = torch.empty(fq.shape[0], fq.shape[1], dtype=torch.float32, device=dev)
+        fneed = A.attn_decode_workspace_bytes(f8_shape.B, f8_shape.Hq, f8_shape.Hkv, f8_shape.d, f8_shape.page_size,
+                                              f8_in.block_table.shape[1], 0)
+        fws = torch.empty(fneed, dtype=torch.uint8, device=dev)
+        fscale = synth.fp32_scale(f8_shape.d)
+        work["decode_fp8"] = lambda: A.attn_decode_paged_fp8(fq, fkc, fvc, f8_in.k_scale, f8_in.v_scale, fbt, fsl,
+                                                             out=fout, lse=flse, scale=fscale, workspace=fws)
     flush_buf = torch.empty(512 << 20, dtype=torch.uint8, device=dev) if args.flush else None
 
     names = list(work)
@@ -377,6 +417,13 @@ def main():
         parts["varlen"] = {"ms": round(ms["varlen"], 4), "ms_min": round(min(per["varlen"]), 4),
                            "tflops": round(flops / t / 1e12, 1), "frac_of_peak": round(flops / t / PEAK_BF16_FLOPS, 4),
                            "flops_per_launch": flops}
+    if f8_shape is not None:
+        nbytes = f8_in.algorithmic_bytes()
+        t = ms["decode_fp8"] / 1e3
+        at_peak += nbytes / PEAK_HBM_BYTES
+        parts["decode_fp8"] = {"ms": round(ms["decode_fp8"], 4), "ms_min": round(min(per["decode_fp8"]), 4),
+                               "gbps": round(nbytes / t / 1e9, 1), "frac_of_peak": round(nbytes / t / PEAK_HBM_BYTES, 4),
+                               "bytes_per_launch": nbytes, "kernels": "stream (FP8 form) + combine"}
     if app_shape is not None:
         nbytes = app_in.algorithmic_bytes()
         t = ms["append"] / 1e3
@@ -395,6 +442,13 @@ def main():
                 "achieved": parts[dom]["tflops"], "peak": PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s",
                 "frac": round(parts[dom]["tflops"] * 1e12 / PEAK_BF16_FLOPS, 4),
                 "traffic": measured_traffic(args.workload, "prefill_bf16_kernel", src), "source_hash": src}
+    elif dom == "decode_fp8":
+        src = kernel_source_hash(["decode_paged.hip", "device_common.h"])
+        roof = {"kernel": "decode_stream_kernel+decode_combine_kernel (FP8 form)", "bound": "hbm",
+                "achieved": parts["decode_fp8"]["gbps"], "peak": PEAK_HBM_BYTES / 1e9, "unit": "GB/s",
+                "frac": round(parts["decode_fp8"]["gbps"] * 1e9 / PEAK_HBM_BYTES, 4),
+                "traffic": measured_traffic(args.workload, "decode_stream_kernel+decode_combine_kernel", src),
+                "source_hash": src}
     elif dom == "append":
         src = kernel_source_hash(["kv_append.hip", "device_common.h"])
         roof = {"kernel": "kv_append_kernel", "bound": "hbm", "achieved": parts["append"]["gbps"],
@@ -415,6 +469,10 @@ def main():
     if dec_inputs is not None:
         cfg["seed_decode"] = 100 + args.workload
         cfg["decode_tokens"] = int(dec_inputs.seq_lens.sum())
+    if f8_in is not None:
+        cfg["seed_decode"] = 100 + args.workload
+        cfg["decode_tokens"] = int(f8_in.seq_lens.sum())
+        cfg["kv_format"] = "FP8 E4M3, per-tensor scales"
     if var_in is not None:
         cfg["seed_varlen"] = args.workload
         cfg["varlen_lens"] = (var_in[3][1:] - var_in[3][:-1]).tolist()
@@ -442,6 +500,8 @@ def main():
         result["cpu_baseline"] = cpu_baseline_chunk(chunk_in)
     if not args.no_cpu_baseline and args.workload == 7:
         result["cpu_baseline"] = cpu_baseline_append(app_in)
+    if not args.no_cpu_baseline and args.workload == 9:
+        result["cpu_baseline"] = cpu_baseline_fp8(f8_in)
     if not args.no_cpu_baseline and args.workload == 8:
         result["cpu_baseline"] = cpu_baseline_varlen(var_in, var_shape)
     print(json.dumps(result), flush=True)
