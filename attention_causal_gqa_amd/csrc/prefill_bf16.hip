@@ -26,9 +26,11 @@
 //     A operand (V^T) comes from transposing ds_read_b64_tr_b16 reads.
 //   * K and V tiles are stored unpadded with an XOR swizzle of 16-byte
 //     chunks, so both operand read patterns are free of bank conflicts.
-//   * out is normalised by the sum of the same bf16-rounded probabilities
-//     that feed the PV product (v_dot2 with ones), so the weights applied to
-//     V sum exactly to the normaliser; the log-sum-exp uses the fp32 sum.
+//   * One row sum, over the fp32 probabilities, normalises out and gives
+//     the log-sum-exp.  The PV product takes the probabilities rounded to
+//     bf16, so the weights applied to V sum to 1 within 2^-9 relative (a
+//     second sum over the rounded values would make that exact, at 20 more
+//     VALU instructions per tile on the critical softmax phase).
 //   * The running max is only moved when a tile's max exceeds it by more
 //     than 8 (a factor 256 in base 2): rescaling O is then rare, and
 //     probabilities stay below 256, well inside fp32 and bf16 range.  The
@@ -291,13 +293,11 @@ __global__ __launch_bounds__(512, 1) void prefill_bf16_kernel(const bf16* __rest
     f32x16 sacc[2];           // S^T of the current tile (64 keys x 32 query columns)
     uint32_t pb[2][2][4];     // P^T of the previous tile in bf16 (B operand of PV)
     float m_run = -INFINITY;  // running max, base-2 scaled domain
-    float l_run = 0.f;        // this lane's share of the row sum of bf16-rounded p (normalises out)
-    float l_lse = 0.f;        // the same sum over fp32 p (for the log-sum-exp)
+    float l_run = 0.f;        // this lane's share of the row sum of p (fp32)
 
     const float cc = kPosScale ? c1 : 1.f;
     const int ntiles = (kend + kBN - 1) / kBN;
     const int first_diag = (pos0 + t0 + 1) / kBN;  // tiles from here on reach past row t0's position
-    constexpr uint32_t kOnes = 0x3F803F80u;  // two bf16 1.0
 
     // MFMA phase: O^T += V^T(t-1) P^T(t-1), then S^T(t) = K(t) Q^T.
     auto mfma_phase = [&](bool do_pv, const char* Vp, bool do_qk, const char* Kc) __attribute__((always_inline)) {
@@ -415,7 +415,6 @@ __global__ __launch_bounds__(512, 1) void prefill_bf16_kernel(const bf16* __rest
             const float mn = grow ? mt : m_run;
             const float alpha = fast_exp2(m_run - mn);
             l_run *= alpha;
-            l_lse *= alpha;
 #pragma unroll
             for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
@@ -426,11 +425,9 @@ __global__ __launch_bounds__(512, 1) void prefill_bf16_kernel(const bf16* __rest
 #pragma unroll
                 for (int i = 0; i < 16; ++i) pf[kb][i] = fast_exp2(fmaf(sacc[kb][i], cc, -m_run));
         }
-        // P^T in bf16: B operand of the PV product.  Two row sums: over the
-        // rounded values (so the weights applied to V sum exactly to the
-        // normaliser of out) and over the fp32 values (the log-sum-exp, which
-        // bf16 rounding of p would otherwise shift by up to 2^-9 relative).
-        float lr[4] = {0.f, 0.f, 0.f, 0.f}, lsum[4] = {0.f, 0.f, 0.f, 0.f};
+        // P^T in bf16: B operand of the PV product; the row sum over the
+        // fp32 values.
+        float lsum[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -440,11 +437,9 @@ __global__ __launch_bounds__(512, 1) void prefill_bf16_kernel(const bf16* __rest
                     const float p0 = pf[kb][8 * kc + 2 * jj];
                     const float p1 = pf[kb][8 * kc + 2 * jj + 1];
                     pb[kb][kc][jj] = pack_bf16x2(p0, p1);
-                    lr[jj] = dot2_bf16(pb[kb][kc][jj], kOnes, lr[jj]);
                     lsum[jj] += p0 + p1;
                 }
-        l_run += (lr[0] + lr[1]) + (lr[2] + lr[3]);
-        l_lse += (lsum[0] + lsum[1]) + (lsum[2] + lsum[3]);
+        l_run += (lsum[0] + lsum[1]) + (lsum[2] + lsum[3]);
     };
 
     // Prologue: the block table (paged form), K(0) from group A; then group
@@ -484,9 +479,8 @@ __global__ __launch_bounds__(512, 1) void prefill_bf16_kernel(const bf16* __rest
     }
     if (grp == 0) __syncthreads();  // matches group B's offset barrier
 
-    // Epilogue: lanes l and l^32 hold halves of the row sums.
+    // Epilogue: lanes l and l^32 hold halves of the row sum.
     const float lt = pair_sum(l_run);
-    const float ll = pair_sum(l_lse);
     if (row_ok) {
         const float inv = 1.f / lt;
         bf16* orow = (kVarlen ? out + ((tok0 + token) * Hq + head) * D
@@ -501,7 +495,7 @@ __global__ __launch_bounds__(512, 1) void prefill_bf16_kernel(const bf16* __rest
                 *reinterpret_cast<u32x2*>(orow + 32 * mb + 8 * g4) = wv;
             }
         if (lse != nullptr && hi == 0)
-            lse[kVarlen ? (tok0 + token) * Hq + head : (size_t)(b * Hq + head) * T + token] = (m_run + log2f(ll)) * kLn2;
+            lse[kVarlen ? (tok0 + token) * Hq + head : (size_t)(b * Hq + head) * T + token] = (m_run + log2f(lt)) * kLn2;
     }
 }
 
