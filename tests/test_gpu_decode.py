@@ -165,3 +165,13 @@ def test_workspace_reuse_and_explicit_workspace():
     with pytest.raises(A.AttnError) as ei:
         A.attn_decode_paged(q, kp, vp, bt, sl, workspace=ws[: need - 256])
     assert ei.value.status == A.ATTN_ERR_WORKSPACE
+
+
+@pytest.mark.parametrize("num_splits", [0, 1])
+def test_longest_context(num_splits):
+    """A sequence of 131072 tokens (8192 pages) beside a shorter one, with the automatic plan and with a
+    single split (one wave streams a whole (sequence, kv head) run)."""
+    lens = [131072, 99999]
+    shp = synth.DecodeShape(len(lens), 8, 2, 128, 16, 1, 131072, torch.bfloat16)
+    inp = synth.paged_inputs(shp, seed=17, seq_lens=lens, poison=float("nan"))
+    check(inp, synth.fp32_scale(128), f"contexts up to 131072 tokens, splits={num_splits}", num_splits=num_splits)

@@ -129,3 +129,13 @@ def test_workload6_sampled():
     inp = synth.chunk_inputs(shp, seed=6)
     rows = sorted(set([0, 1, 63, 64, 255, 256, 1023, shp.Tq - 2, shp.Tq - 1]))
     check(inp, synth.fp32_scale(shp.d), "workload 6 (B4 Hq32 Hkv8 Tq2048 L~U[4096,16384])", rows=rows)
+
+
+def test_longest_supported_context():
+    """Contexts of 131072 tokens: the whole 8192-entry block table the kernel stages in LDS is in use
+    (the longest context the chunked prefill accepts), once with a ragged last page."""
+    lens = [131072, 131072 - 5]
+    shp = synth.ChunkShape(len(lens), 8, 2, 64, 128, synth.PAGE_SIZE, 1, 131072, BF16)
+    inp = synth.chunk_inputs(shp, seed=131, seq_lens=lens, poison=float("nan"))
+    assert inp.block_table.shape[1] == 8192
+    check(inp, synth.fp32_scale(128), "contexts of 131072 tokens (8192 pages)", rows=[0, 1, 31, 62, 63])
