@@ -1,4 +1,5 @@
-"""Build libattn.so (the C-ABI library) in-tree with hipcc for gfx950.
+"""Build libattn.so (the C-ABI library) in-tree with hipcc for gfx950, and the
+benchmark's read-bandwidth probe, libattn_probe.so.
 
     python -m attention_causal_gqa_amd.build        # or: python attention_causal_gqa_amd/build.py
 
@@ -20,6 +21,9 @@ LIB = os.path.join(PKG, "libattn.so")
 ARCH = "gfx950"
 
 SOURCES = ["attn_api.cpp", "prefill_f32.hip", "prefill_bf16.hip", "decode_paged.hip", "kv_append.hip"]
+# The benchmark's read-bandwidth probe: a library of its own, outside the C ABI.
+PROBE_SOURCES = ["probe_read.hip"]
+PROBE_LIB = os.path.join(PKG, "libattn_probe.so")
 
 # Per-source extra flags.  The bf16 prefill's softmax sees only finite scores
 # and -inf (never NaN: inputs are finite by contract), so NaN-quieting
@@ -144,7 +148,7 @@ def build(verbose=False):
     os.makedirs(BUILD, exist_ok=True)
     cc = hipcc()
     jobs = []
-    for src in SOURCES:
+    for src in SOURCES + PROBE_SOURCES:
         obj = os.path.join(BUILD, src.rsplit(".", 1)[0] + ".o")
         jobs.append((src, obj, [cc, *FLAGS, *EXTRA_FLAGS.get(src, []), "-Rpass-analysis=kernel-resource-usage", "-c",
                                 os.path.join(CSRC, src), "-o", obj]))
@@ -165,11 +169,13 @@ def build(verbose=False):
         raise RuntimeError("kernels use scratch memory: " + "; ".join(scratch))
     for src in ASM_LOAD_SOURCES:
         _check_asm_loads(cc, src)
-    tmp = LIB + ".tmp"
-    rc, out = _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *[j[1] for j in jobs], "-o", tmp])
-    if rc != 0:
-        raise RuntimeError("link failed:\n" + out)
-    os.replace(tmp, LIB)
+    for lib, srcs in ((LIB, SOURCES), (PROBE_LIB, PROBE_SOURCES)):
+        tmp = lib + ".tmp"
+        objs = [j[1] for j in jobs if j[0] in srcs]
+        rc, out = _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp])
+        if rc != 0:
+            raise RuntimeError(f"link of {os.path.basename(lib)} failed:\n" + out)
+        os.replace(tmp, lib)
     return LIB
 
 

@@ -59,6 +59,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--flush", action="store_true",
                    help="read a 512 MiB buffer before each step (outside the kernel events) to evict L2/MALL")
+    p.add_argument("--read-ceiling", action="store_true",
+                   help="only time plain reads: a 2 GiB buffer, and workload 5's K/V page slices in decode order")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 1 GiB device-to-device copy ten times (reference for the HBM byte counters)")
     return p.parse_args()
@@ -78,6 +80,63 @@ def copy_calibration():
     torch.cuda.synchronize()
     print(json.dumps({"copy_calibration": {"bytes_read_per_launch": COPY_BYTES, "bytes_written_per_launch": COPY_BYTES,
                                            "launches": 10}}), flush=True)
+
+
+def read_ceiling(args):
+    """The practical HBM read ceiling: a kernel that only reads (libattn_probe.so), timed with HIP events
+    over K launches, on (1) a 2 GiB buffer in 4 KiB slices and (2) the 4 KiB K and V slices of workload
+    5's decode pool, (sequence, kv head, page) in the streaming decode's order, from a pool far larger
+    than the MALL.  Context for the decode's rate, not a replacement for the 8 TB/s peak."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "attention_causal_gqa_amd", "libattn_probe.so"))
+    vp = ctypes.c_void_p
+    lib.probe_read_slices.argtypes = [vp, vp, ctypes.c_longlong, ctypes.c_int, vp, ctypes.c_int, vp]
+    lib.probe_read_slices.restype = ctypes.c_int
+    dev = torch.device("cuda:0")
+    blocks = torch.cuda.get_device_properties(dev).multi_processor_count * 8
+    sink = torch.zeros(256, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+    slice_bytes = 4096
+
+    def timed(base, offs, n):
+        def go():
+            rc = lib.probe_read_slices(base.data_ptr(), None if offs is None else offs.data_ptr(), n, slice_bytes,
+                                       sink.data_ptr(), blocks, ctypes.c_void_p(stream.cuda_stream))
+            if rc != 0:
+                raise RuntimeError(f"probe_read_slices failed: {rc}")
+        for _ in range(args.warmup):
+            go()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            go()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.steps
+        return ms, n * slice_bytes / (ms / 1e3) / 1e9
+
+    big = torch.ones(2 << 30, dtype=torch.uint8, device=dev)
+    c_ms, c_gbps = timed(big, None, big.numel() // slice_bytes)
+    del big
+    shp = synth.WORKLOADS[5]["decode"]
+    inp = synth.paged_inputs(shp, seed=105)
+    P, Hkv = inp.k_pages.shape[0], shp.Hkv
+    pool = torch.ones(2 * P * Hkv * slice_bytes, dtype=torch.uint8, device=dev)  # K pool, then V pool
+    offs = []
+    for b in range(shp.B):
+        n = (int(inp.seq_lens[b]) + shp.page_size - 1) // shp.page_size
+        pages = inp.block_table[b, :n].long()
+        for kvh in range(Hkv):
+            ko = (pages * Hkv + kvh) * slice_bytes
+            offs.append(torch.stack([ko, ko + P * Hkv * slice_bytes], dim=1).reshape(-1))
+    offs = torch.cat(offs).to(dev)
+    p_ms, p_gbps = timed(pool, offs, offs.numel())
+    print(json.dumps({"read_ceiling": {
+        "contiguous": {"bytes": 2 << 30, "ms": round(c_ms, 4), "gbps": round(c_gbps, 1)},
+        "decode_pages_w5": {"slices": int(offs.numel()), "bytes": int(offs.numel()) * slice_bytes, "ms": round(p_ms, 4),
+                            "gbps": round(p_gbps, 1)},
+        "blocks": blocks, "slice_bytes": slice_bytes, "steps": args.steps}}), flush=True)
 
 
 def kernel_source_hash(names):
@@ -259,6 +318,9 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.read_ceiling:
+        read_ceiling(args)
         return
     dev = torch.device("cuda:0")
     A.load_library()

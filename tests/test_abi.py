@@ -327,3 +327,21 @@ def test_asm_load_guard_flags_early_use():
     assert not _asm_load_hazards(head + "\tglobal_load_dword v9, v[2:3], off\n\ts_waitcnt vmcnt(1)\n"
                                         "\tv_add_f32_e32 v1, v1, v2\n\ts_waitcnt vmcnt(0)\n\tv_mov_b32_e32 v1, v9\n")
     assert not _asm_load_hazards(head + "\ts_waitcnt vmcnt(0)\n\tv_mov_b32_e32 v34, v50\n")
+
+
+def test_read_probe_library_loads_and_rejects_bad_arguments():
+    """The benchmark's read-bandwidth probe (a library of its own, outside the C ABI) is built beside
+    libattn.so; its argument checks run before any HIP call."""
+    import ctypes
+    import os
+    probe = ctypes.CDLL(os.path.join(os.path.dirname(A.__file__), "libattn_probe.so"))
+    f = probe.probe_read_slices
+    vp = ctypes.c_void_p
+    f.argtypes = [vp, vp, ctypes.c_longlong, ctypes.c_int, vp, ctypes.c_int, vp]
+    f.restype = ctypes.c_int
+    good = dict(base=FAKE, offs=None, n=4, slice_bytes=4096, sink=FAKE, blocks=8)
+    for bad in (dict(base=None), dict(sink=None), dict(n=-1), dict(slice_bytes=8), dict(slice_bytes=4100),
+                dict(slice_bytes=8192), dict(blocks=0)):
+        a = {**good, **bad}
+        assert f(a["base"], a["offs"], a["n"], a["slice_bytes"], a["sink"], a["blocks"], None) != 0, bad
+    assert f(FAKE, None, 0, 4096, FAKE, 8, None) == 0  # nothing to read: no launch
