@@ -16,7 +16,11 @@ GPU runs a short sleep kernel, so that the events time kernels rather than
 host launch latency.  A workload with a single part times its K queued
 launches between one pair of events instead (``ms_min`` stays per launch).
 
-    python bench.py [--steps K] [--warmup W] [--workload 5|3|4|6|7|8|9] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--workload 5|3|4|6|7|8|9] [--no-cpu-baseline] [--flush]
+
+``--flush`` reads a 512 MiB buffer before every step (outside the events),
+so that a decode whose K/V would fit in the 256 MB MALL (workload 4) starts
+cold; ``value`` then comes from the kernels' event time.
 
 Workload 6 (not the default) times the chunked prefill over a paged cache:
 2048-token chunks at the end of four sequences of 4096..16384 cached tokens.
@@ -25,6 +29,7 @@ Workload 8 times the ragged prefill of 16 sequences of 256..4096 tokens
 packed along the token axis.  Workload 9 times the paged decode of workload
 5 over an FP8 E4M3 cache (algorithmic bytes: one byte per cached value).
     python bench.py --copy-calibration   # plain 1 GiB copy, reference for HBM byte counters
+    python bench.py --read-ceiling       # plain reads: 2 GiB, and workload 5's decode slices
 """
 
 import argparse

@@ -1,7 +1,7 @@
 /*
  * attn.h — causal multi-head / grouped-query attention for MI355X (gfx950).
  *
- * Two operations, both hand-written HIP kernels behind a plain C ABI:
+ * Six operations, all hand-written HIP kernels behind a plain C ABI:
  *
  *  - attn_prefill: causal self-attention of T queries over the same T keys,
  *    computed block by block with an online softmax so that the T x T score
