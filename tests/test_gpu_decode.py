@@ -175,3 +175,26 @@ def test_longest_context(num_splits):
     shp = synth.DecodeShape(len(lens), 8, 2, 128, 16, 1, 131072, torch.bfloat16)
     inp = synth.paged_inputs(shp, seed=17, seq_lens=lens, poison=float("nan"))
     check(inp, synth.fp32_scale(128), f"contexts up to 131072 tokens, splits={num_splits}", num_splits=num_splits)
+
+
+@pytest.mark.parametrize("slope", [0.25, 0.1, -0.25])
+def test_running_max_moves_across_pages(slope):
+    """Cached keys whose scores rise (or fall) with the position: component 0 of the key at position j is
+    j * slope and every query is (8, small noise), so with slope 0.25 the running max of a split moves on
+    every page group, with 0.1 only on some, with -0.25 never after the first."""
+    shp = synth.DecodeShape(3, 8, 2, 128, 16, 1, 1500, torch.bfloat16)
+    inp = synth.paged_inputs(shp, seed=29, seq_lens=[1500, 777, 64], poison=float("nan"))
+    g = torch.Generator().manual_seed(30)
+    q = 0.05 * torch.randn(inp.q.shape, generator=g)
+    q[..., 0] = 8.0
+    inp.q = q.to(torch.bfloat16)
+    kp = inp.k_pages.float()
+    for b in range(3):
+        L = int(inp.seq_lens[b])
+        pos = torch.arange(L)
+        pages = inp.block_table[b, pos // 16].long()
+        kp[pages, :, pos % 16, :] = 0.05 * torch.randn(L, shp.Hkv, shp.d, generator=g)
+        kp[pages, :, pos % 16, 0] = (slope * pos.float())[:, None]
+    inp.k_pages = kp.to(torch.bfloat16)
+    for splits in (0, 1):
+        check(inp, synth.fp32_scale(128), f"score ramp, slope {slope}, splits={splits}", num_splits=splits)

@@ -180,3 +180,26 @@ def test_full_size_prefill_sampled(workload):
     assert (out.float().abs().amax(dim=(2, 3)) <= vmax * (1 + 2.0**-8)).all()
     s0 = scale * (q.float() * k.float()[:, :, :1].repeat_interleave(shp.Hq // shp.Hkv, dim=1)).sum(-1)
     assert (lse >= s0 - 1e-3).all()
+
+
+# ------------------------------------------------------------------ the lazy running-max rescale
+def ramp_inputs(B, Hq, Hkv, T, d, slope, seed, dtype=torch.bfloat16):
+    """Scores that rise (slope > 0) or fall along the keys: component 0 of key j is j * slope, every query is
+    (8, small noise); other key components are small noise.  With scale 1/sqrt(d) the base-2 score of key j
+    is about 1.02 * slope * j (d = 128)."""
+    g = torch.Generator().manual_seed(seed)
+    q = 0.05 * torch.randn(B, Hq, T, d, generator=g)
+    q[..., 0] = 8.0
+    k = 0.05 * torch.randn(B, Hkv, T, d, generator=g)
+    k[..., 0] = slope * torch.arange(T, dtype=torch.float32)
+    v = torch.randn(B, Hkv, T, d, generator=g)
+    return q.to(dtype), k.to(dtype), v.to(dtype)
+
+
+@pytest.mark.parametrize("slope", [0.25, 0.1, -0.25])
+def test_running_max_moves_across_tiles(slope):
+    """slope 0.25: each 64-key tile's max exceeds the previous one by about 16 (base 2), so the running max
+    and the output rescale move in every tile; 0.1: about 6.5 per tile, so they move in some tiles and not
+    in others (probabilities up to 2^8 against a stale max); -0.25: the max is key 0's and never moves."""
+    q, k, v = ramp_inputs(1, 8, 2, 520, 128, slope, seed=31)
+    check_full(q, k, v, synth.fp32_scale(128), TOL_BF16, f"bf16 score ramp, slope {slope}")
