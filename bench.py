@@ -1,10 +1,13 @@
 """Benchmark of the attention hot path on one MI355X.
 
 One step = one pass of the whole path over the mixed long-context workload:
-causal GQA prefill (B1 Hq32 Hkv8 T8192 d128, bf16) followed by paged
-single-token decode (B64 Hq32 Hkv8 d128, page 16, seq_lens ~ U[1024, 8192]),
-i.e. the prefill kernel, the split-KV decode kernel and the LSE combine
-kernel.  Inputs are seeded synthetic tensors, resident in HBM before timing.
+causal GQA prefill (B1 Hq32 Hkv8 T8192 d128, bf16) and paged single-token
+decode (B64 Hq32 Hkv8 d128, page 16, seq_lens ~ U[1024, 8192]), i.e. the
+prefill kernel, the split-KV decode kernel and the LSE combine kernel.  The
+two parts are independent, so by default they run on two HIP streams (the
+HBM-bound decode launched first, beside the MFMA-bound prefill) joined once
+per step; ``--sequential`` runs them one after the other.  Inputs are seeded
+synthetic tensors, resident in HBM before timing.
 
 Prints one JSON line.  ``value`` is the step's roofline fraction: the time the
 step's algorithmic work takes at MI355X peak (prefill flops at the bf16 MFMA
@@ -62,6 +65,9 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", type=int, default=5, choices=(3, 4, 5, 6, 7, 8, 9))
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--sequential", action="store_true",
+                   help="run the parts of a two-part step (workload 5) one after the other on one stream; by default "
+                        "the decode and the prefill run on two HIP streams, joined once per step")
     p.add_argument("--flush", action="store_true",
                    help="read a 512 MiB buffer before each step (outside the kernel events) to evict L2/MALL")
     p.add_argument("--read-ceiling", action="store_true",
@@ -402,43 +408,80 @@ def main():
 
     names = list(work)
     stream = torch.cuda.current_stream()
+    # A two-part step (prefill of new tokens, decode of running sequences:
+    # independent work) runs its parts on two HIP streams by default, the
+    # HBM-bound decode launched first, so that it overlaps the MFMA-bound
+    # prefill; the step ends when both are done.  Default stream priority.
+    concurrent = len(names) > 1 and not args.sequential
+    order = sorted(names, key=lambda n: 0 if n == "decode" else 1) if concurrent else names
+    part_streams = {n: torch.cuda.Stream() for n in names} if concurrent else {}
+    start_ev = torch.cuda.Event()
+    done_ev = {n: torch.cuda.Event() for n in names}
 
-    def step(events=None):
+    def step(events=None, seq=False):
+        """One step; events: {part: (start, end)} plus "step": (start, end), recorded if given."""
         if flush_buf is not None:
             torch.sum(flush_buf, dim=0, out=flush_sink)
-        for i, n in enumerate(names):
-            if events is not None:
-                events[i].record(stream)
-            work[n]()
         if events is not None:
-            events[len(names)].record(stream)
+            events["step"][0].record(stream)
+        if not concurrent or seq:
+            for n in names:
+                if events is not None:
+                    events[n][0].record(stream)
+                work[n]()
+                if events is not None:
+                    events[n][1].record(stream)
+        else:
+            start_ev.record(stream)
+            for n in order:
+                ps = part_streams[n]
+                ps.wait_event(start_ev)
+                with torch.cuda.stream(ps):
+                    if events is not None:
+                        events[n][0].record(ps)
+                    work[n]()
+                    if events is not None:
+                        events[n][1].record(ps)
+                done_ev[n].record(ps)
+            for n in order:
+                stream.wait_event(done_ev[n])
+        if events is not None:
+            events["step"][1].record(stream)
+
+    def new_events():
+        return {n: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                for n in names + ["step"]}
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    # Timed region A (the step rate): K steps between two synchronizations,
-    # host clock.
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-
     # Timed region B (per-kernel times): the same K steps with HIP events
     # around each part, on the launch stream.  A GPU-side sleep first lets
     # the host queue all K steps, so the events time the kernels and not the
     # host's marshalling and launch latency (which exceeds a short decode).
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
+    # With two streams each part's events sit on its own stream, so a part's
+    # time is its duration inside the concurrent step.
+    evs = [new_events() for _ in range(args.steps)]
     torch.cuda.synchronize()
     torch.cuda._sleep(200_000 * args.steps)
     for s in range(args.steps):
         step(evs[s])
     torch.cuda.synchronize()
 
-    per = {n: [evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(args.steps)] for i, n in enumerate(names)}
+    per = {n: [evs[s][n][0].elapsed_time(evs[s][n][1]) for s in range(args.steps)] for n in names}
     ms = {n: float(np.mean(per[n])) for n in names}
+    step_ms = float(np.mean([evs[s]["step"][0].elapsed_time(evs[s]["step"][1]) for s in range(args.steps)]))
+    ms_alone = None
+    if concurrent:  # each part alone (one after the other), for reference
+        evs2 = [new_events() for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        torch.cuda._sleep(200_000 * args.steps)
+        for s in range(args.steps):
+            step(evs2[s], seq=True)
+        torch.cuda.synchronize()
+        ms_alone = {n: float(np.mean([evs2[s][n][0].elapsed_time(evs2[s][n][1]) for s in range(args.steps)]))
+                    for n in names}
     if len(names) == 1 and flush_buf is None:
         # One part per step: time the K queued launches between one pair of
         # events, so that a short kernel's time does not carry the cost of an
@@ -453,7 +496,26 @@ def main():
         e1.record(stream)
         torch.cuda.synchronize()
         ms[names[0]] = e0.elapsed_time(e1) / args.steps
-    kernel_ms = sum(ms.values())
+    # Timed region A (the step rate): K steps between two synchronizations,
+    # host clock.  It runs after the event passes, which leave the GPU in the
+    # steady state of a running loop (its clock takes some tens of steps to
+    # settle after the process starts).
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    wall_seq = None
+    if concurrent:  # the same K steps with the parts one after the other, for reference
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            step(seq=True)
+        torch.cuda.synchronize()
+        wall_seq = time.perf_counter() - t0
+
+    kernel_ms = step_ms if len(names) > 1 else sum(ms.values())
     ms_per_step = wall * 1e3 / args.steps
 
     result = {"metric": METRIC}
@@ -509,6 +571,10 @@ def main():
     # write, which is not part of the path: the step is then the kernels'
     # event time.
     value = at_peak / ((kernel_ms if flush_buf is not None else ms_per_step) / 1e3)
+    if ms_alone is not None:
+        for n, pt in parts.items():
+            pt["ms_alone"] = round(ms_alone[n], 4)
+            pt["frac_of_peak_alone"] = round(pt["frac_of_peak"] * ms[n] / ms_alone[n], 4)
 
     # Dominant kernel's roofline (the one with the larger share of the step).
     dom = max(names, key=lambda n: ms[n])
@@ -539,6 +605,15 @@ def main():
                 "frac": round(parts["decode"]["gbps"] * 1e9 / PEAK_HBM_BYTES, 4),
                 "traffic": measured_traffic(args.workload, "decode_stream_kernel+decode_combine_kernel", src),
                 "source_hash": src}
+    if ms_alone is not None:
+        # With two streams the parts share the chip and their durations in
+        # the step overlap; the kernel's own rate is its duration when it runs
+        # alone (measured in this run, one part after the other).
+        r = ms[dom] / ms_alone[dom]
+        roof["achieved_in_step"] = roof["achieved"]
+        roof["achieved"] = round(roof["achieved"] * r, 1)
+        roof["frac"] = round(roof["frac"] * r, 4)
+        roof["timed_alone"] = True
 
     cfg = {"workload": synth.WORKLOAD_NAMES[args.workload]}
     if pre_shape is not None:
@@ -565,6 +640,8 @@ def main():
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4),
         "kernel_ms_per_step": round(kernel_ms, 4),
+        **({"schedule": "decode and prefill on two HIP streams, joined once per step",
+            "ms_per_step_sequential": round(wall_seq * 1e3 / args.steps, 4)} if concurrent else {}),
         **({"flush": "512 MiB read before each step (outside the kernel events); value from kernel_ms_per_step"}
            if flush_buf is not None else {}),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
