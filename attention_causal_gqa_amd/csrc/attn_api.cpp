@@ -130,8 +130,10 @@ int attn_prefill(const void* q, const void* k, const void* v, void* out, float* 
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16))
         return fail(ATTN_ERR_INVALID_ARG, "q, k, v and out must be 16-byte aligned");
     if (lse && !aligned(lse, 4)) return fail(ATTN_ERR_INVALID_ARG, "lse must be 4-byte aligned");
-    // Grid and element counts must fit the kernels' index arithmetic.
-    const int64_t rows_per_block = dtype == ATTN_F32 ? 64 : (128 / (Hq / Hkv));
+    // The launch grid must fit the kernels' int index arithmetic: the fp32
+    // kernel takes 64 rows of one head per workgroup, the bf16 kernel 256
+    // (token, head) rows of one kv group.
+    const int64_t rows_per_block = dtype == ATTN_F32 ? 64 : (256 / (Hq / Hkv));
     const int64_t nqb = (T + rows_per_block - 1) / rows_per_block;
     const int64_t blocks = nqb * B * (dtype == ATTN_F32 ? Hq : Hkv);
     if (blocks > kMaxGrid) return fail(ATTN_ERR_INVALID_ARG, "problem too large: %lld workgroups", (long long)blocks);
