@@ -427,7 +427,7 @@ __global__ __launch_bounds__(512, 1) void prefill_bf16_kernel(const bf16* __rest
         }
         // P^T in bf16: B operand of the PV product; the row sum over the
         // fp32 values.
-        float lsum[4] = {0.f, 0.f, 0.f, 0.f};
+        float lsum[4];  // started from the first pair: no additions of zero
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -437,7 +437,7 @@ __global__ __launch_bounds__(512, 1) void prefill_bf16_kernel(const bf16* __rest
                     const float p0 = pf[kb][8 * kc + 2 * jj];
                     const float p1 = pf[kb][8 * kc + 2 * jj + 1];
                     pb[kb][kc][jj] = pack_bf16x2(p0, p1);
-                    lsum[jj] += p0 + p1;
+                    lsum[jj] = kb == 0 && kc == 0 ? p0 + p1 : lsum[jj] + (p0 + p1);
                 }
         l_run += (lsum[0] + lsum[1]) + (lsum[2] + lsum[3]);
     };
