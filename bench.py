@@ -17,7 +17,8 @@ Per-kernel rates come from HIP events recorded on the launch stream around
 each part, in a second pass of K steps whose launches are queued while the
 GPU runs a short sleep kernel, so that the events time kernels rather than
 host launch latency.  A workload with a single part times its K queued
-launches between one pair of events instead (``ms_min`` stays per launch).
+launches between one pair of events instead.  ``ms_min``, ``ms_median`` and
+``ms_p90`` of each part are always over the per-step event pairs.
 
     python bench.py [--steps K] [--warmup W] [--workload 5|3|4|6|7|8|9] [--no-cpu-baseline] [--flush]
 
@@ -518,6 +519,12 @@ def main():
     kernel_ms = step_ms if len(names) > 1 else sum(ms.values())
     ms_per_step = wall * 1e3 / args.steps
 
+    def spread(n):
+        """Min, median and 90th percentile of a part's per-step event times (timed region B)."""
+        x = np.asarray(per[n])
+        return {"ms_min": round(float(x.min()), 4), "ms_median": round(float(np.median(x)), 4),
+                "ms_p90": round(float(np.percentile(x, 90)), 4)}
+
     result = {"metric": METRIC}
     at_peak = 0.0
     parts = {}
@@ -525,14 +532,14 @@ def main():
         flops = pre_shape.flops()
         t = ms["prefill"] / 1e3
         at_peak += flops / PEAK_BF16_FLOPS
-        parts["prefill"] = {"ms": round(ms["prefill"], 4), "ms_min": round(min(per["prefill"]), 4),
+        parts["prefill"] = {"ms": round(ms["prefill"], 4), **spread("prefill"),
                             "tflops": round(flops / t / 1e12, 1), "frac_of_peak": round(flops / t / PEAK_BF16_FLOPS, 4),
                             "flops_per_launch": flops}
     if dec_shape is not None:
         nbytes = dec_inputs.algorithmic_bytes()
         t = ms["decode"] / 1e3
         at_peak += nbytes / PEAK_HBM_BYTES
-        parts["decode"] = {"ms": round(ms["decode"], 4), "ms_min": round(min(per["decode"]), 4),
+        parts["decode"] = {"ms": round(ms["decode"], 4), **spread("decode"),
                            "gbps": round(nbytes / t / 1e9, 1), "frac_of_peak": round(nbytes / t / PEAK_HBM_BYTES, 4),
                            "bytes_per_launch": nbytes, "kernels": "stream + combine",
                            "num_splits": A.attn_decode_num_splits(dec_shape.B, dec_shape.Hq, dec_shape.Hkv,
@@ -542,7 +549,7 @@ def main():
         flops = synth.chunk_flops(chunk_shape.Hq, chunk_shape.d, chunk_shape.Tq, chunk_in.seq_lens.tolist())
         t = ms["chunk"] / 1e3
         at_peak += flops / PEAK_BF16_FLOPS
-        parts["chunk"] = {"ms": round(ms["chunk"], 4), "ms_min": round(min(per["chunk"]), 4),
+        parts["chunk"] = {"ms": round(ms["chunk"], 4), **spread("chunk"),
                           "tflops": round(flops / t / 1e12, 1), "frac_of_peak": round(flops / t / PEAK_BF16_FLOPS, 4),
                           "flops_per_launch": flops}
     if var_shape is not None:
@@ -550,21 +557,21 @@ def main():
         flops = synth.varlen_flops(var_shape.Hq, var_shape.d, lens)
         t = ms["varlen"] / 1e3
         at_peak += flops / PEAK_BF16_FLOPS
-        parts["varlen"] = {"ms": round(ms["varlen"], 4), "ms_min": round(min(per["varlen"]), 4),
+        parts["varlen"] = {"ms": round(ms["varlen"], 4), **spread("varlen"),
                            "tflops": round(flops / t / 1e12, 1), "frac_of_peak": round(flops / t / PEAK_BF16_FLOPS, 4),
                            "flops_per_launch": flops}
     if f8_shape is not None:
         nbytes = f8_in.algorithmic_bytes()
         t = ms["decode_fp8"] / 1e3
         at_peak += nbytes / PEAK_HBM_BYTES
-        parts["decode_fp8"] = {"ms": round(ms["decode_fp8"], 4), "ms_min": round(min(per["decode_fp8"]), 4),
+        parts["decode_fp8"] = {"ms": round(ms["decode_fp8"], 4), **spread("decode_fp8"),
                                "gbps": round(nbytes / t / 1e9, 1), "frac_of_peak": round(nbytes / t / PEAK_HBM_BYTES, 4),
                                "bytes_per_launch": nbytes, "kernels": "stream (FP8 form) + combine"}
     if app_shape is not None:
         nbytes = app_in.algorithmic_bytes()
         t = ms["append"] / 1e3
         at_peak += nbytes / PEAK_HBM_BYTES
-        parts["append"] = {"ms": round(ms["append"], 4), "ms_min": round(min(per["append"]), 4),
+        parts["append"] = {"ms": round(ms["append"], 4), **spread("append"),
                            "gbps": round(nbytes / t / 1e9, 1), "frac_of_peak": round(nbytes / t / PEAK_HBM_BYTES, 4),
                            "bytes_per_launch": nbytes}
     # With --flush the host-clock step includes the 512 MiB cache-evicting
