@@ -513,6 +513,13 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(const float* __restr
     const int bh = blockIdx.x;
     const int b = bh / Hq;
     const int lane = threadIdx.x;
+    const float* lp = lse_part + (size_t)bh * S;
+    const float* op = o_part + (size_t)bh * S * D;
+    // The first 128 slot values are loaded beside the sequence length (any
+    // slot below S may be read; those past the sequence's own are dropped
+    // once its length is known) and kept for both passes.
+    const float r0 = lane < S ? lp[lane] : -INFINITY;
+    const float r1 = 64 + lane < S ? lp[64 + lane] : -INFINITY;
     const int L = seq_lens[b];
     bf16* orow = out + (size_t)bh * D;
     if (L == 0) {
@@ -522,13 +529,11 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(const float* __restr
         return;
     }
     const int ns = ((L + kPage - 1) / kPage + pps - 1) / pps;
-    const float* lp = lse_part + (size_t)bh * S;
-    const float* op = o_part + (size_t)bh * S * D;
-    float M = -INFINITY;
-    for (int c0 = 0; c0 < ns; c0 += 64) {
-        const int s = c0 + lane;
-        if (s < ns) M = fmaxf(M, lp[s]);
-    }
+    auto slot_lse = [&](int s) __attribute__((always_inline)) {
+        return s >= ns ? -INFINITY : s < 64 ? r0 : s < 128 ? r1 : lp[s];
+    };
+    float M = fmaxf(slot_lse(lane), slot_lse(64 + lane));
+    for (int c0 = 128; c0 < ns; c0 += 64) M = fmaxf(M, slot_lse(c0 + lane));
     M = wave_max(M);  // finite: slot 0 always starts a piece
     float acc[NDW];
 #pragma unroll
@@ -536,7 +541,7 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(const float* __restr
     float wsum = 0.f;
     for (int c0 = 0; c0 < ns; c0 += 64) {
         const int s = c0 + lane;
-        const float l = s < ns ? lp[s] : -INFINITY;
+        const float l = slot_lse(s);
         const float wt = fast_exp2((l - M) * kLog2e);  // 0 for non-pieces
         wsum += wt;
         unsigned long long mask = __ballot(l != -INFINITY);

@@ -53,18 +53,4 @@ __device__ __forceinline__ float pair_sum(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Sum over the 16 lanes of a DPP row; every lane of the row gets the total.
-template <typename T>
-__device__ __forceinline__ T dpp_row_sum16(T x);
-
-template <>
-__device__ __forceinline__ float dpp_row_sum16<float>(float x) {
-    // quad_perm [1,0,3,2] (xor 1), quad_perm [2,3,0,1] (xor 2), row_ror 4, row_ror 8
-    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));
-    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));
-    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x124, 0xF, 0xF, false));
-    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false));
-    return x;
-}
-
 }  // namespace attn
