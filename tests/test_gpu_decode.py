@@ -177,6 +177,19 @@ def test_longest_context(num_splits):
     check(inp, synth.fp32_scale(128), f"contexts up to 131072 tokens, splits={num_splits}", num_splits=num_splits)
 
 
+def test_combine_slot_counts_at_register_boundaries():
+    """With one page per item, sequences of 64, 65, 128 and 129 pages give the combine exactly 64, 65, 128
+    and 129 slots: the combine holds the first 128 slot values in registers and reads any later ones, so
+    the pieces on both sides of slots 64 and 128 are merged by both paths."""
+    lens = [1024, 1025, 2048, 2049]
+    shp = synth.DecodeShape(len(lens), 4, 2, 128, 16, 1, 2049, torch.bfloat16)
+    inp = synth.paged_inputs(shp, seed=31, seq_lens=lens, poison=float("nan"))
+    W = inp.max_pages_per_seq
+    assert A.attn_decode_num_splits(shp.B, shp.Hq, shp.Hkv, shp.d, shp.page_size, W, 0) == W  # one page per item
+    for ns in (0, 1, 3):
+        check(inp, synth.fp32_scale(128), f"combine slot counts 64/65/128/129, splits={ns}", num_splits=ns)
+
+
 @pytest.mark.parametrize("slope", [0.25, 0.1, -0.25])
 def test_running_max_moves_across_pages(slope):
     """Cached keys whose scores rise (or fall) with the position: component 0 of the key at position j is
