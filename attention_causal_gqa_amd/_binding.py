@@ -7,6 +7,7 @@ none, and raises ``AttnError`` on a non-zero status.  If the library is not
 built, every call raises: there is no other path.
 """
 
+import contextlib
 import ctypes
 import math
 import os
@@ -112,6 +113,19 @@ def _stream(stream):
     return _torch().cuda.current_stream().cuda_stream
 
 
+def _alloc_stream(stream):
+    """Context in which torch allocates on the stream the kernels run on.
+
+    Outputs and workspaces allocated here belong to that stream in torch's
+    caching allocator, so a block released after the call is reused only by
+    later work on the same stream, which runs after these kernels."""
+    if stream is None:
+        return contextlib.nullcontext()
+    torch = _torch()
+    s = torch.cuda.ExternalStream(stream) if isinstance(stream, int) else stream
+    return torch.cuda.stream(s)
+
+
 def _require(cond, msg):
     if not cond:
         raise AttnError(ATTN_ERR_INVALID_ARG, msg)
@@ -132,10 +146,11 @@ def attn_prefill(q, k, v, out=None, lse=None, scale=None, stream=None):
     _require(q.dtype == k.dtype == v.dtype, "q, k, v must share a dtype")
     for n, t in (("q", q), ("k", k), ("v", v)):
         _dense_on_gpu(n, t)
-    if out is None:
-        out = torch.empty_like(q)
-    if lse is None:
-        lse = torch.empty((B, Hq, T), dtype=torch.float32, device=q.device)
+    with _alloc_stream(stream):
+        if out is None:
+            out = torch.empty_like(q)
+        if lse is None:
+            lse = torch.empty((B, Hq, T), dtype=torch.float32, device=q.device)
     _dense_on_gpu("out", out)
     _require(out.shape == q.shape and out.dtype == q.dtype, "out must match q")
     if lse is not False:
@@ -165,10 +180,11 @@ def attn_prefill_paged(q, k_pages, v_pages, block_table, seq_lens, out=None, lse
         _dense_on_gpu(n, t)
     _require(q.dtype == k_pages.dtype == v_pages.dtype, "q and the page pools must share a dtype")
     W = block_table.shape[1]
-    if out is None:
-        out = torch.empty_like(q)
-    if lse is None:
-        lse = torch.empty((B, Hq, Tq), dtype=torch.float32, device=q.device)
+    with _alloc_stream(stream):
+        if out is None:
+            out = torch.empty_like(q)
+        if lse is None:
+            lse = torch.empty((B, Hq, Tq), dtype=torch.float32, device=q.device)
     _dense_on_gpu("out", out)
     _require(out.shape == q.shape and out.dtype == q.dtype, "out must match q")
     if lse is not False:
@@ -196,10 +212,11 @@ def attn_prefill_varlen(q, k, v, cu_seqlens, max_seqlen, out=None, lse=None, sca
     for n, t in (("q", q), ("k", k), ("v", v), ("cu_seqlens", cu_seqlens)):
         _dense_on_gpu(n, t)
     _require(q.dtype == k.dtype == v.dtype, "q, k, v must share a dtype")
-    if out is None:
-        out = torch.empty_like(q)
-    if lse is None:
-        lse = torch.empty((N, Hq), dtype=torch.float32, device=q.device)
+    with _alloc_stream(stream):
+        if out is None:
+            out = torch.empty_like(q)
+        if lse is None:
+            lse = torch.empty((N, Hq), dtype=torch.float32, device=q.device)
     _dense_on_gpu("out", out)
     _require(out.shape == q.shape and out.dtype == q.dtype, "out must match q")
     if lse is not False:
@@ -261,10 +278,11 @@ def attn_decode_paged(q, k_pages, v_pages, block_table, seq_lens, out=None, lse=
         _dense_on_gpu(n, t)
     _require(q.dtype == k_pages.dtype == v_pages.dtype, "q and the page pools must share a dtype")
     W = block_table.shape[1]
-    if out is None:
-        out = torch.empty_like(q)
-    if lse is None:
-        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    with _alloc_stream(stream):
+        if out is None:
+            out = torch.empty_like(q)
+        if lse is None:
+            lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
     _dense_on_gpu("out", out)
     _require(out.shape == q.shape and out.dtype == q.dtype, "out must match q")
     if lse is not False:
@@ -275,7 +293,8 @@ def attn_decode_paged(q, k_pages, v_pages, block_table, seq_lens, out=None, lse=
     lib = load_library()
     need = lib.attn_decode_workspace_bytes(B, Hq, Hkv, d, page_size, W, num_splits)
     if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+        with _alloc_stream(stream):
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     _dense_on_gpu("workspace", workspace)
     ws_bytes = workspace.numel() * workspace.element_size()
     _check(lib.attn_decode_paged(_ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table), _ptr(seq_lens), _ptr(out),
@@ -304,10 +323,11 @@ def attn_decode_paged_fp8(q, k_pages, v_pages, k_scale, v_scale, block_table, se
                  ("seq_lens", seq_lens)):
         _dense_on_gpu(n, t)
     W = block_table.shape[1]
-    if out is None:
-        out = torch.empty_like(q)
-    if lse is None:
-        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    with _alloc_stream(stream):
+        if out is None:
+            out = torch.empty_like(q)
+        if lse is None:
+            lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
     _dense_on_gpu("out", out)
     _require(out.shape == q.shape and out.dtype == q.dtype, "out must match q")
     if lse is not False:
@@ -318,7 +338,8 @@ def attn_decode_paged_fp8(q, k_pages, v_pages, k_scale, v_scale, block_table, se
     lib = load_library()
     need = lib.attn_decode_workspace_bytes(B, Hq, Hkv, d, page_size, W, num_splits)
     if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+        with _alloc_stream(stream):
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     _dense_on_gpu("workspace", workspace)
     ws_bytes = workspace.numel() * workspace.element_size()
     _check(lib.attn_decode_paged_fp8(_ptr(q), _ptr(k_pages), _ptr(v_pages), float(k_scale), float(v_scale),

@@ -75,9 +75,26 @@ Plan make_plan(int B, int Hkv, int W, int num_splits) {
 
 size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-size_t workspace_for(int B, int Hq, int d, const Plan& p) {
-    const size_t n = (size_t)B * Hq * p.splits;
-    return round256(n * d * sizeof(float)) + round256(n * sizeof(float));
+// Decode workspace: the streaming kernel stores the piece of run r (sequence
+// b, kv head j: r = b * Hkv + j) met by wave w in slot r + w, so there are
+// fewer than B * Hkv + kMaxStreamWaves slots, each holding G = Hq / Hkv
+// partial rows of d fp32 values and G fp32 log-sum-exps; after them, one
+// record of four int32 per run (first slot, piece count, and where the
+// pieces lie: the run's offset in its first wave's share and the share size).  The size does not depend on the
+// sequence lengths or the split plan.
+struct WorkspaceLayout {
+    size_t o_part, lse_part, run_info, bytes;  // byte offsets, total
+};
+
+WorkspaceLayout workspace_layout(int B, int Hq, int Hkv, int d) {
+    const size_t runs = (size_t)B * Hkv;
+    const size_t rows = (runs + attn::kMaxStreamWaves) * (size_t)(Hq / Hkv);
+    WorkspaceLayout w{};
+    w.o_part = 0;
+    w.lse_part = round256(rows * d * sizeof(float));
+    w.run_info = w.lse_part + round256(rows * sizeof(float));
+    w.bytes = w.run_info + round256(runs * 4 * sizeof(int));
+    return w;
 }
 
 int check_decode_sizes(int B, int Hq, int Hkv, int d, int page_size, int W, int num_splits) {
@@ -93,6 +110,45 @@ int check_decode_sizes(int B, int Hq, int Hkv, int d, int page_size, int W, int 
     if (page_size != kPageSize) return fail(ATTN_ERR_UNSUPPORTED, "decode supports page_size = 16, not %d", page_size);
     if (Hq / Hkv > kMaxDecodeGroup)
         return fail(ATTN_ERR_UNSUPPORTED, "decode supports Hq/Hkv <= %d, not %d", kMaxDecodeGroup, Hq / Hkv);
+    // The kernels index the flattened (sequence, kv head, page) stream and the
+    // run records with 32-bit offsets.
+    if ((int64_t)B * Hkv * W > 0x7fffffff)
+        return fail(ATTN_ERR_UNSUPPORTED, "decode supports B * Hkv * max_pages_per_seq < 2^31, not %lld",
+                    (long long)B * Hkv * W);
+    return ATTN_OK;
+}
+
+// The launch arguments of a validated decode call: the split plan and the
+// workspace carved into its three regions.
+int decode_args(const void* q, const void* k_pages, const void* v_pages, const int32_t* block_table,
+                const int32_t* seq_lens, void* out, float* lse, int B, int Hq, int Hkv, int d, int page_size, int W,
+                float scale, int num_splits, void* workspace, size_t workspace_bytes, attn::DecodeArgs* a) {
+    if ((int64_t)B * Hq > kMaxGrid) return fail(ATTN_ERR_INVALID_ARG, "problem too large");
+    const WorkspaceLayout lay = workspace_layout(B, Hq, Hkv, d);
+    if (!workspace || workspace_bytes < lay.bytes)
+        return fail(ATTN_ERR_WORKSPACE, "workspace %zu bytes given, %zu needed", workspace ? workspace_bytes : 0,
+                    lay.bytes);
+    if (!aligned(workspace, 16)) return fail(ATTN_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+    char* ws = static_cast<char*>(workspace);
+    const Plan plan = make_plan(B, Hkv, W, num_splits);
+    *a = attn::DecodeArgs{q,
+                          k_pages,
+                          v_pages,
+                          block_table,
+                          seq_lens,
+                          out,
+                          lse,
+                          reinterpret_cast<float*>(ws + lay.o_part),
+                          reinterpret_cast<float*>(ws + lay.lse_part),
+                          reinterpret_cast<int*>(ws + lay.run_info),
+                          B,
+                          Hq,
+                          Hkv,
+                          d,
+                          page_size,
+                          W,
+                          plan.pages_per_split,
+                          scale};
     return ATTN_OK;
 }
 
@@ -274,7 +330,7 @@ size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int d, int page_size,
                                    int num_splits) {
     g_last_error.clear();
     if (check_decode_sizes(B, Hq, Hkv, d, page_size, max_pages_per_seq, num_splits) != ATTN_OK) return 0;
-    return workspace_for(B, Hq, d, make_plan(B, Hkv, max_pages_per_seq, num_splits));
+    return workspace_layout(B, Hq, Hkv, d).bytes;
 }
 
 int attn_decode_paged(const void* q, const void* k_pages, const void* v_pages, const int32_t* block_table,
@@ -296,19 +352,10 @@ int attn_decode_paged(const void* q, const void* k_pages, const void* v_pages, c
     if (!aligned(block_table, 4) || !aligned(seq_lens, 4) || (lse && !aligned(lse, 4)))
         return fail(ATTN_ERR_INVALID_ARG, "block_table, seq_lens and lse must be 4-byte aligned");
 
-    const Plan plan = make_plan(B, Hkv, max_pages_per_seq, num_splits);
-    if ((int64_t)B * Hq > kMaxGrid) return fail(ATTN_ERR_INVALID_ARG, "problem too large");
-    const size_t need = workspace_for(B, Hq, d, plan);
-    if (!workspace || workspace_bytes < need)
-        return fail(ATTN_ERR_WORKSPACE, "workspace %zu bytes given, %zu needed", workspace ? workspace_bytes : 0, need);
-    if (!aligned(workspace, 16)) return fail(ATTN_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
-
-    const size_t n = (size_t)B * Hq * plan.splits;
-    float* o_part = static_cast<float*>(workspace);
-    float* lse_part = reinterpret_cast<float*>(static_cast<char*>(workspace) + round256(n * d * sizeof(float)));
-    attn::DecodeArgs a{q,      k_pages,  v_pages, block_table, seq_lens, out, lse, o_part, lse_part, B,
-                       Hq,     Hkv,      d,       page_size,   max_pages_per_seq, plan.splits,
-                       plan.pages_per_split, scale};
+    attn::DecodeArgs a{};
+    st = decode_args(q, k_pages, v_pages, block_table, seq_lens, out, lse, B, Hq, Hkv, d, page_size,
+                     max_pages_per_seq, scale, num_splits, workspace, workspace_bytes, &a);
+    if (st != ATTN_OK) return st;
     return from_hip(attn::launch_decode_bf16(a, stream), "attn_decode_paged launch");
 }
 
@@ -330,18 +377,10 @@ int attn_decode_paged_fp8(const void* q, const void* k_pages, const void* v_page
         return fail(ATTN_ERR_INVALID_ARG, "q, k_pages, v_pages and out must be 16-byte aligned");
     if (!aligned(block_table, 4) || !aligned(seq_lens, 4) || (lse && !aligned(lse, 4)))
         return fail(ATTN_ERR_INVALID_ARG, "block_table, seq_lens and lse must be 4-byte aligned");
-    const Plan plan = make_plan(B, Hkv, max_pages_per_seq, num_splits);
-    if ((int64_t)B * Hq > kMaxGrid) return fail(ATTN_ERR_INVALID_ARG, "problem too large");
-    const size_t need = workspace_for(B, Hq, d, plan);
-    if (!workspace || workspace_bytes < need)
-        return fail(ATTN_ERR_WORKSPACE, "workspace %zu bytes given, %zu needed", workspace ? workspace_bytes : 0, need);
-    if (!aligned(workspace, 16)) return fail(ATTN_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
-    const size_t n = (size_t)B * Hq * plan.splits;
-    float* o_part = static_cast<float*>(workspace);
-    float* lse_part = reinterpret_cast<float*>(static_cast<char*>(workspace) + round256(n * d * sizeof(float)));
-    attn::DecodeArgs a{q,      k_pages,  v_pages, block_table, seq_lens, out, lse, o_part, lse_part, B,
-                       Hq,     Hkv,      d,       page_size,   max_pages_per_seq, plan.splits,
-                       plan.pages_per_split, scale};
+    attn::DecodeArgs a{};
+    st = decode_args(q, k_pages, v_pages, block_table, seq_lens, out, lse, B, Hq, Hkv, d, page_size,
+                     max_pages_per_seq, scale, num_splits, workspace, workspace_bytes, &a);
+    if (st != ATTN_OK) return st;
     return from_hip(attn::launch_decode_fp8(a, k_scale, v_scale, stream), "attn_decode_paged_fp8 launch");
 }
 

@@ -14,8 +14,8 @@
 // kv group are handled together (16x16 MFMA tiles, G columns used), so each
 // K/V byte is read once for the whole group.  Each run of pages of one
 // (sequence, kv head) that a wave meets is one piece; its normalised partial
-// output and log-sum-exp go to the workspace slot of the piece's first item
-// (a fixed run of pages_per_split pages).
+// output and log-sum-exp go to a workspace slot of its own, or, when the
+// piece is the whole run, straight to the output.
 //
 // FP8 form (kFp8): the pools hold FP8 E4M3 codes with one scale per tensor
 // (the FP8 KV cache of the microLLM-rocm README, "Why this project exists";
@@ -121,29 +121,41 @@ struct Cursor {
 
 __device__ __forceinline__ int pages_of(int L) { return (L + kPage - 1) / kPage; }
 
+__device__ __forceinline__ long long readlane64(long long v, int src) {
+    const int lo = __builtin_amdgcn_readlane((int)(unsigned long long)v, src);
+    const int hi = __builtin_amdgcn_readlane((int)((unsigned long long)v >> 32), src);
+    return (long long)(((unsigned long long)(unsigned)hi << 32) | (unsigned)lo);
+}
+
 // Inclusive prefix sum over the 64 lanes of a wave.
-__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
+__device__ __forceinline__ long long wave_incl_scan(long long v, int lane) {
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
-        const int t = __shfl_up(v, o);
+        const long long t = __shfl_up(v, o);
         if (lane >= o) v += t;
     }
     return v;
 }
 
 // Streaming split kernel: one wave per workgroup, as many workgroups as fit
-// on the chip at once.  The work is the flattened stream of all
-// (sequence, kv head, page) triples (Hkv * sum_b ceil(L_b / 16) pages); wave
-// w takes the pages from snap(w C) up to snap((w + 1) C), C = ceil(total /
-// waves), where snap moves an offset up to the next item start.  An item is
-// a run of pps pages of one (sequence, kv head) beginning at a multiple of
-// pps, so every wave gets C pages give or take pps, whatever the mix of
-// lengths, and a sequence's keys are cut only at item starts.
+// on the chip at once (at most kMaxStreamWaves).  The work is the flattened
+// stream of all (sequence, kv head, page) triples (Hkv * sum_b ceil(L_b /
+// 16) pages); wave w takes the pages from snap(w C) up to snap((w + 1) C),
+// C = ceil(total / waves), where snap moves an offset up to the next item
+// start.  An item is a run of pps pages of one (sequence, kv head) beginning
+// at a multiple of pps, so every wave gets C pages give or take pps,
+// whatever the mix of lengths, and a sequence's keys are cut only at item
+// starts.  An item starting at offset e belongs to wave floor(e / C).
 //
 // A wave keeps one online softmax per (sequence, kv head) run it meets (a
-// piece) and writes it, normalised, with its log-sum-exp into the slot of
-// the piece's first item; the piece's other item slots get lse = -inf as
-// the wave reaches them, and the combine kernel skips those.  Per page (16 tokens) and wave:
+// piece).  The pieces of run r (r = b * Hkv + kv head) belong to consecutive
+// waves w_first .. w_last, and the piece of wave w is stored in workspace
+// slot r + w: along the stream either r or w grows from one piece to the
+// next, so slots are distinct, and there are fewer than B * Hkv + waves of
+// them.  The wave that meets a run's first page records (first slot, piece
+// count) for the combine kernel; a run that lies inside one wave is
+// normalised and written to out / lse directly (piece count recorded as 0).
+// Per page (16 tokens) and wave:
 //   S^T = K Q^T   (16 tokens x 16 head columns; v_mfma_f32_16x16x32_bf16,
 //                  K read from HBM straight into the A-operand layout, the G
 //                  query heads of the kv group in the B columns, zero-padded)
@@ -158,9 +170,10 @@ __global__ __launch_bounds__(64) void decode_stream_kernel(const bf16* __restric
                                                             const char* __restrict__ vp,
                                                             const int32_t* __restrict__ block_table,
                                                             const int32_t* __restrict__ seq_lens,
+                                                            bf16* __restrict__ out, float* __restrict__ lse,
                                                             float* __restrict__ o_part, float* __restrict__ lse_part,
-                                                            int B, int Hq, int Hkv, int G, int W, int S, int pps,
-                                                            float c1, float vscale) {
+                                                            int* __restrict__ run_info, int B, int Hq, int Hkv, int G,
+                                                            int W, int pps, float c1, float vscale) {
     constexpr int NKK = D / 32;        // k-steps of QK^T (16x16x32)
     constexpr int NB = D / 16;         // 16-column blocks of O (16x16x16)
     constexpr int ROWB = D * 2;        // bytes per token row in bf16 (the LDS layout of V)
@@ -180,60 +193,74 @@ __global__ __launch_bounds__(64) void decode_stream_kernel(const bf16* __restric
     const int lane = threadIdx.x;
     const int hd = lane & 15;  // head column (S^T, P) / d within a 16-block (O)
     const int g = lane >> 4;   // 16-lane row: tokens 4g..4g+3 (S^T, P) / head rows 4g..4g+3 (O)
+    const int wv = blockIdx.x;
 
     // ---- this wave's share of the page stream
-    // Sequences are taken 64 at a time, one per lane: token count, page
-    // count and inclusive prefix of page counts.  The first 64 stay in
-    // registers (with B <= 64 nothing is read twice).
-    int L0 = 0, n0 = 0, i0 = 0;
-    long long total = 0;
-    for (int c0 = 0; c0 < B; c0 += 64) {
-        const int bb = c0 + lane;
-        const int Lb = bb < B ? seq_lens[bb] : 0;
-        const int n = pages_of(Lb);
-        const int incl = wave_incl_scan(n, lane);
-        if (c0 == 0) {
-            L0 = Lb;
-            n0 = n;
-            i0 = incl;
+    // Lane l sums the pages of the contiguous block of sequences
+    // [l per, (l + 1) per), per = ceil(B / 64); a scan over the lanes gives
+    // each block's first offset.  All of a lane's loads are independent, so
+    // the whole pass is one round trip to memory, whatever B is.
+    const int per = (B + 63) >> 6;
+    const int blk0 = min(B, lane * per);
+    const int blk1 = min(B, blk0 + per);
+    int Lself = 0;  // per == 1: this lane's own sequence length
+    long long sblk = 0;
+    if (per == 1) {
+        Lself = blk0 < blk1 ? seq_lens[blk0] : 0;
+        sblk = pages_of(Lself);
+    } else {
+        for (int i = blk0; i < blk1; i += 4) {
+            int lv[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) lv[u] = i + u < blk1 ? seq_lens[i + u] : 0;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) sblk += pages_of(lv[u]);
         }
-        total += __builtin_amdgcn_readlane(incl, 63);
     }
-    total *= Hkv;
+    const long long iblk = wave_incl_scan(sblk, lane);
+    const long long total = readlane64(iblk, 63) * Hkv;
     const long long C = (total + gridDim.x - 1) / gridDim.x;
-    const long long xa = (long long)blockIdx.x * C;
+    const long long xa = (long long)wv * C;
     if (xa >= total) return;
     const long long xb = xa + C < total ? xa + C : total;
 
     // Cursor at snap(x), x < total; c.j may equal c.n (then the item start
     // is the next run's first page, see normalize).
     auto locate = [&](long long x, Cursor& c) __attribute__((always_inline)) {
-        long long carry = 0;  // pages of the sequences before this chunk
-        for (int c0 = 0; c0 < B; c0 += 64) {
-            int Lb = L0, n = n0, incl = i0;
-            if (c0 != 0) {
+        // the lane block holding x, then the sequence within it
+        const unsigned long long hit = __ballot(sblk > 0 && (iblk - sblk) * Hkv <= x && x < iblk * Hkv);
+        const int src = __builtin_ctzll(hit);
+        long long base = readlane64(iblk - sblk, src);  // pages of the sequences before the block
+        if (per == 1) {
+            c.b = src;
+            c.L = __builtin_amdgcn_readlane(Lself, src);
+            c.n = pages_of(c.L);
+        } else {
+            const int e1 = min(B, src * per + per);
+            for (int c0 = src * per; c0 < e1; c0 += 64) {
                 const int bb = c0 + lane;
-                Lb = bb < B ? seq_lens[bb] : 0;
-                n = pages_of(Lb);
-                incl = wave_incl_scan(n, lane);
+                const int Lb = bb < e1 ? seq_lens[bb] : 0;
+                const int n = pages_of(Lb);
+                const long long inc = wave_incl_scan((long long)n, lane);
+                const long long e = (base + inc - n) * Hkv;
+                const unsigned long long h2 = __ballot(n > 0 && e <= x && x < e + (long long)n * Hkv);
+                if (h2) {
+                    const int s2 = __builtin_ctzll(h2);
+                    c.b = c0 + s2;
+                    c.n = __builtin_amdgcn_readlane(n, s2);
+                    c.L = __builtin_amdgcn_readlane(Lb, s2);
+                    base += readlane64(inc, s2) - c.n;
+                    break;
+                }
+                base += readlane64(inc, 63);
             }
-            const long long e = (carry + incl - n) * Hkv;  // flattened offset of sequence c0 + lane
-            const unsigned long long hit = __ballot(n > 0 && e <= x && x < e + (long long)n * Hkv);
-            if (hit) {
-                const int src = __builtin_ctzll(hit);
-                c.b = c0 + src;
-                c.n = __builtin_amdgcn_readlane(n, src);
-                c.L = __builtin_amdgcn_readlane(Lb, src);
-                const long long eb = (carry + __builtin_amdgcn_readlane(incl, src) - c.n) * Hkv;
-                const int r = (int)(x - eb);
-                c.kvh = r / c.n;
-                const int jr = (r % c.n + pps - 1) / pps * pps;
-                c.j = jr < c.n ? jr : c.n;
-                c.x = eb + (long long)c.kvh * c.n + c.j;
-                return;
-            }
-            carry += __builtin_amdgcn_readlane(incl, 63);
         }
+        const long long eb = base * Hkv;  // flattened offset of sequence c.b
+        const int r = (int)(x - eb);
+        c.kvh = r / c.n;
+        const int jr = (r % c.n + pps - 1) / pps * pps;
+        c.j = jr < c.n ? jr : c.n;
+        c.x = eb + (long long)c.kvh * c.n + c.j;
     };
     // Move a cursor with j == n to the next run's first page.  Only called
     // when c.x < total, so a non-empty sequence follows.
@@ -335,13 +362,13 @@ __global__ __launch_bounds__(64) void decode_stream_kernel(const bf16* __restric
             for (int i = 0; i < NCH; ++i) {
                 const int n = lane + 64 * i;
                 const int r = n / CPR, cc = n % CPR;
-                u32x4 wv = {0u, 0u, 0u, 0u};
+                u32x4 wv4 = {0u, 0u, 0u, 0u};
                 if (r < nvalid) {
                     const u32x2 f = *reinterpret_cast<const u32x2*>(vslot + r * KROWB + 8 * cc);
                     const u32x2 a = fp8x4_to_bf16(f.x), b2 = fp8x4_to_bf16(f.y);
-                    wv = u32x4{a.x, a.y, b2.x, b2.y};
+                    wv4 = u32x4{a.x, a.y, b2.x, b2.y};
                 }
-                *reinterpret_cast<u32x4*>(Vw + r * ROWB + 16 * (cc ^ vswz<D>(r))) = wv;
+                *reinterpret_cast<u32x4*>(Vw + r * ROWB + 16 * (cc ^ vswz<D>(r))) = wv4;
             }
             vbuf = Vw;
         } else if (nvalid < kPage) {
@@ -408,26 +435,39 @@ __global__ __launch_bounds__(64) void decode_stream_kernel(const bf16* __restric
         }
     };
 
-    // Current piece: its (sequence, kv head) and first item slot.
-    int pb = 0, pkvh = 0, ps0 = 0;
+    // Current piece: its (sequence, kv head), and whether it is its run's
+    // only piece (then it is the final result).
+    int pb = 0, pkvh = 0;
+    bool psingle = false;
     auto flush = [&]() __attribute__((always_inline)) {
         // Row sums: add the four 16-lane rows (tokens 4g..4g+3).
         const float lr = pair_sum(row_pair_sum(l_run));
         const float ll = pair_sum(row_pair_sum(l_lse));
         const float inv = vscale / lr;
+        const float lse_v = (m_run + log2f(ll)) * kLn2;
         const size_t bh0 = (size_t)pb * Hq + (size_t)pkvh * G;
+        const size_t slot = (size_t)pb * Hkv + pkvh + wv;
         // lane holds O[head 4g + i][16nb + hd]
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int head = 4 * g + i;
             const float ih = __shfl(inv, head);
             if (head < G) {
-                float* dst = o_part + ((bh0 + head) * S + ps0) * D + hd;
+                if (psingle) {
+                    bf16* dst = out + (bh0 + head) * D + hd;
 #pragma unroll
-                for (int nb = 0; nb < NB; ++nb) dst[16 * nb] = oacc[nb][i] * ih;
+                    for (int nb = 0; nb < NB; ++nb) dst[16 * nb] = (bf16)(oacc[nb][i] * ih);
+                } else {
+                    float* dst = o_part + (slot * G + head) * D + hd;
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb) dst[16 * nb] = oacc[nb][i] * ih;
+                }
             }
         }
-        if (g == 0 && hd < G) lse_part[(bh0 + hd) * S + ps0] = (m_run + log2f(ll)) * kLn2;
+        if (g == 0 && hd < G) {
+            if (!psingle) lse_part[slot * G + hd] = lse_v;
+            else if (lse != nullptr) lse[bh0 + hd] = lse_v;
+        }
     };
 
     // Page loop, unrolled by two over two (K registers, V buffer) sets: the
@@ -464,11 +504,25 @@ __global__ __launch_bounds__(64) void decode_stream_kernel(const bf16* __restric
             reset();
             pb = cc.b;
             pkvh = cc.kvh;
-            ps0 = cc.j / pps;
-        } else if (cc.j % pps == 0 && lane < G) {
-            // a later item of the piece: mark its slot (one store per page
-            // at most, so the loads in flight stay countable)
-            lse_part[((size_t)pb * Hq + (size_t)pkvh * G + lane) * S + cc.j / pps] = -INFINITY;
+            if (cc.j == 0) {
+                // The run starts here, at x = cc.x (its first item belongs to
+                // this wave).  Its K items start at x + k pps and belong to
+                // waves floor((x + k pps) / C): with pps < C these are every
+                // wave from wv to that of the last item, with pps >= C one
+                // wave per item.  One store, so the loads in flight stay
+                // countable.
+                const int K = (cc.n + pps - 1) / pps;
+                const long long e_last = cc.x + (long long)(K - 1) * pps;
+                const int npieces = pps >= C ? K : (int)(e_last / C) - wv + 1;
+                psingle = npieces == 1;
+                if (lane == 0) {
+                    const int r = cc.b * Hkv + cc.kvh;
+                    *reinterpret_cast<int4*>(run_info + 4 * (size_t)r) =
+                        int4{r + wv, psingle ? 0 : npieces, (int)(cc.x - (long long)wv * C), (int)C};
+                }
+            } else {
+                psingle = false;
+            }
         }
         compute_page(cc, kx, bx);
         cc = cf;
@@ -494,33 +548,34 @@ __device__ __forceinline__ float wave_sum(float x) {
     return x;
 }
 
-// Combine kernel: one wave per (sequence, query head).  The sequence's item
-// slots hold either a piece's normalised partial output and log-sum-exp or
-// lse = -inf (an item that continues a piece; its o_part is never written).
-// Pieces are merged with weights exp(lse_i - max lse) (block-wise softmax
-// statistics, llm-from-scratch "Project Overview", "Performance Layer:
-// kernel/ and parallel/").  Slot lse values are read 64 at a time, one per
-// lane; the pieces among them are found by ballot and their partial rows
-// are loaded eight at a time, so the loads overlap.
+// Combine kernel: one wave per (sequence, query head).  The split kernel
+// records, per run, its first slot, its piece count (0: the run was one
+// piece, already written to out / lse), the offset o of the run's first item
+// within its wave's share, and the share size C.  Piece i is in slot
+// first + i when items are shorter than a share (pps < C), else in slot
+// first + floor((o + i pps) / C) (one wave per item).  Pieces are merged
+// with weights exp(lse_i - max lse) (block-wise softmax statistics,
+// llm-from-scratch "Project Overview", "Performance Layer: kernel/ and
+// parallel/").  The first BATCH partial rows are loaded together with the
+// pieces' lse values, so a run of up to BATCH pieces costs one round trip
+// after the run record.
 template <int D>
 __global__ __launch_bounds__(64) void decode_combine_kernel(const float* __restrict__ o_part,
                                                             const float* __restrict__ lse_part,
+                                                            const int* __restrict__ run_info,
                                                             const int32_t* __restrict__ seq_lens,
                                                             bf16* __restrict__ out, float* __restrict__ lse, int Hq,
-                                                            int S, int pps) {
+                                                            int Hkv, int G, int pps) {
     constexpr int NDW = D / 64;  // d values per lane
     constexpr int BATCH = 8;
     const int bh = blockIdx.x;
     const int b = bh / Hq;
+    const int h = bh % Hq;
+    const int r = b * Hkv + h / G;
+    const int hh = h % G;
     const int lane = threadIdx.x;
-    const float* lp = lse_part + (size_t)bh * S;
-    const float* op = o_part + (size_t)bh * S * D;
-    // The first 128 slot values are loaded beside the sequence length (any
-    // slot below S may be read; those past the sequence's own are dropped
-    // once its length is known) and kept for both passes.
-    const float r0 = lane < S ? lp[lane] : -INFINITY;
-    const float r1 = 64 + lane < S ? lp[64 + lane] : -INFINITY;
     const int L = seq_lens[b];
+    const int4 info = *reinterpret_cast<const int4*>(run_info + 4 * (size_t)r);
     bf16* orow = out + (size_t)bh * D;
     if (L == 0) {
 #pragma unroll
@@ -528,47 +583,55 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(const float* __restr
         if (lse != nullptr && lane == 0) lse[bh] = -INFINITY;
         return;
     }
-    const int ns = ((L + kPage - 1) / kPage + pps - 1) / pps;
-    auto slot_lse = [&](int s) __attribute__((always_inline)) {
-        return s >= ns ? -INFINITY : s < 64 ? r0 : s < 128 ? r1 : lp[s];
+    const int first = info.x, count = info.y;
+    if (count == 0) return;  // a single piece: the split kernel wrote the result
+    const unsigned o = (unsigned)info.z, Cs = (unsigned)info.w;
+    const bool itemwise = (unsigned)pps >= Cs;
+    // slot of piece i (i < count); o + i pps < 2^31 + 2^27 fits 32 bits
+    auto slot = [&](int i) __attribute__((always_inline)) {
+        return first + (itemwise ? (int)((o + (unsigned)i * (unsigned)pps) / Cs) : i);
     };
-    float M = fmaxf(slot_lse(lane), slot_lse(64 + lane));
-    for (int c0 = 128; c0 < ns; c0 += 64) M = fmaxf(M, slot_lse(c0 + lane));
-    M = wave_max(M);  // finite: slot 0 always starts a piece
+    // slot s holds head hh's partial row at (s G + hh)
+    const float* lp = lse_part + hh;
+    const float* op = o_part + (size_t)hh * D + lane;
+    const size_t rstride = (size_t)G * D;
+    const float l0 = lane < count ? lp[(size_t)slot(lane) * G] : -INFINITY;
+    float v[BATCH][NDW];
+#pragma unroll
+    for (int u = 0; u < BATCH; ++u) {
+        const size_t row = (size_t)slot(min(u, count - 1));
+#pragma unroll
+        for (int k = 0; k < NDW; ++k) v[u][k] = op[row * rstride + 64 * k];
+    }
+    float M = l0;
+    for (int c0 = 64; c0 < count; c0 += 64)
+        M = fmaxf(M, c0 + lane < count ? lp[(size_t)slot(c0 + lane) * G] : -INFINITY);
+    M = wave_max(M);  // finite: every piece holds at least one token
     float acc[NDW];
 #pragma unroll
     for (int k = 0; k < NDW; ++k) acc[k] = 0.f;
     float wsum = 0.f;
-    for (int c0 = 0; c0 < ns; c0 += 64) {
-        const int s = c0 + lane;
-        const float l = slot_lse(s);
-        const float wt = fast_exp2((l - M) * kLog2e);  // 0 for non-pieces
+    for (int c0 = 0; c0 < count; c0 += 64) {
+        const int n = min(64, count - c0);
+        const float l = c0 == 0 ? l0 : (lane < n ? lp[(size_t)slot(c0 + lane) * G] : -INFINITY);
+        const float wt = fast_exp2((l - M) * kLog2e);  // 0 past the last piece
         wsum += wt;
-        unsigned long long mask = __ballot(l != -INFINITY);
-        const int first = mask ? __builtin_ctzll(mask) : 0;
-        while (mask) {
-            int js[BATCH];
-            float ws[BATCH];
+        for (int u0 = 0; u0 < n; u0 += BATCH) {
+            if (c0 + u0 != 0) {
 #pragma unroll
-            for (int u = 0; u < BATCH; ++u) {
-                if (mask) {
-                    js[u] = __builtin_ctzll(mask);
-                    mask &= mask - 1;
-                    ws[u] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wt), js[u]));
-                } else {
-                    js[u] = first;  // a written slot, weighted 0
-                    ws[u] = 0.f;
+                for (int u = 0; u < BATCH; ++u) {
+                    const size_t row = (size_t)slot(c0 + min(u0 + u, n - 1));
+#pragma unroll
+                    for (int k = 0; k < NDW; ++k) v[u][k] = op[row * rstride + 64 * k];
                 }
             }
-            float v[BATCH][NDW];
 #pragma unroll
-            for (int u = 0; u < BATCH; ++u)
+            for (int u = 0; u < BATCH; ++u) {
+                const float ws = u0 + u < n ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wt), u0 + u))
+                                            : 0.f;
 #pragma unroll
-                for (int k = 0; k < NDW; ++k) v[u][k] = op[(size_t)(c0 + js[u]) * D + 64 * k + lane];
-#pragma unroll
-            for (int u = 0; u < BATCH; ++u)
-#pragma unroll
-                for (int k = 0; k < NDW; ++k) acc[k] = fmaf(ws[u], v[u][k], acc[k]);
+                for (int k = 0; k < NDW; ++k) acc[k] = fmaf(ws, v[u][k], acc[k]);
+            }
         }
     }
     wsum = wave_sum(wsum);
@@ -578,23 +641,30 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(const float* __restr
     if (lse != nullptr && lane == 0) lse[bh] = M + logf(wsum);
 }
 
-// Workgroups of the streaming kernel that are resident at once on the
-// current device (compute units x occupancy), found once per device.
+// Workgroups of the streaming kernel that are resident at once on `dev`
+// (compute units x occupancy, at most kMaxStreamWaves), found once per device.
 template <int D, bool kFp8>
-hipError_t stream_waves(int* nw) {
+hipError_t stream_waves(int dev, int* nw) {
     static std::atomic<int> cache[kMaxDevices];
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return e;
     if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
     int v = cache[dev].load(std::memory_order_relaxed);
     if (v == 0) {
         int cus = 0, per = 0;
+        hipError_t e;
         if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
-        if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, decode_stream_kernel<D, kFp8>, 64, 0)) !=
-            hipSuccess)
-            return e;
+        // The occupancy query reads the current device's properties: run it
+        // with `dev` current.
+        int cur = 0;
+        if ((e = hipGetDevice(&cur)) != hipSuccess) return e;
+        if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, decode_stream_kernel<D, kFp8>, 64, 0);
+        if (cur != dev) {
+            const hipError_t e2 = hipSetDevice(cur);
+            if (e == hipSuccess) e = e2;
+        }
+        if (e != hipSuccess) return e;
         v = cus * (per > 0 ? per : 1);
+        if (v > kMaxStreamWaves) v = kMaxStreamWaves;
         cache[dev].store(v, std::memory_order_relaxed);
     }
     *nw = v;
@@ -602,28 +672,33 @@ hipError_t stream_waves(int* nw) {
 }
 
 template <int D, bool kFp8>
-hipError_t launch_split(const DecodeArgs& a, hipStream_t stream, float c1, float vscale) {
+hipError_t launch_split(const DecodeArgs& a, int dev, hipStream_t stream, float c1, float vscale) {
     int nw = 0;
-    const hipError_t e = stream_waves<D, kFp8>(&nw);
+    const hipError_t e = stream_waves<D, kFp8>(dev, &nw);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((decode_stream_kernel<D, kFp8>), dim3((unsigned)nw), dim3(64), 0, stream, (const bf16*)a.q,
-                       (const char*)a.k_pages, (const char*)a.v_pages, a.block_table, a.seq_lens, a.o_part,
-                       a.lse_part, a.B, a.Hq, a.Hkv, a.Hq / a.Hkv, a.W, a.num_splits, a.pages_per_split, c1, vscale);
+                       (const char*)a.k_pages, (const char*)a.v_pages, a.block_table, a.seq_lens, (bf16*)a.out, a.lse,
+                       a.o_part, a.lse_part, a.run_info, a.B, a.Hq, a.Hkv, a.Hq / a.Hkv, a.W, a.pages_per_split, c1,
+                       vscale);
     return hipGetLastError();
 }
 
 template <bool kFp8>
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream, float kscale, float vscale) {
     const float c1 = (float)((double)a.scale * (double)kscale * 1.4426950408889634);
-    const hipError_t e = a.d == 128 ? launch_split<128, kFp8>(a, stream, c1, vscale)
-                                    : launch_split<64, kFp8>(a, stream, c1, vscale);
+    hipDevice_t dev = 0;
+    hipError_t e = hipStreamGetDevice(stream, &dev);
     if (e != hipSuccess) return e;
+    e = a.d == 128 ? launch_split<128, kFp8>(a, dev, stream, c1, vscale)
+                   : launch_split<64, kFp8>(a, dev, stream, c1, vscale);
+    if (e != hipSuccess) return e;
+    const int G = a.Hq / a.Hkv;
     if (a.d == 128) {
         hipLaunchKernelGGL(decode_combine_kernel<128>, dim3((unsigned)a.B * a.Hq), dim3(64), 0, stream, a.o_part,
-                           a.lse_part, a.seq_lens, (bf16*)a.out, a.lse, a.Hq, a.num_splits, a.pages_per_split);
+                           a.lse_part, a.run_info, a.seq_lens, (bf16*)a.out, a.lse, a.Hq, a.Hkv, G, a.pages_per_split);
     } else {
         hipLaunchKernelGGL(decode_combine_kernel<64>, dim3((unsigned)a.B * a.Hq), dim3(64), 0, stream, a.o_part,
-                           a.lse_part, a.seq_lens, (bf16*)a.out, a.lse, a.Hq, a.num_splits, a.pages_per_split);
+                           a.lse_part, a.run_info, a.seq_lens, (bf16*)a.out, a.lse, a.Hq, a.Hkv, G, a.pages_per_split);
     }
     return hipGetLastError();
 }

@@ -17,6 +17,10 @@ struct PrefillArgs {
     float scale;
 };
 
+// Most one-wave workgroups the streaming decode kernel launches; the
+// workspace has B * Hkv + kMaxStreamWaves piece slots.
+constexpr int kMaxStreamWaves = 4096;
+
 struct DecodeArgs {
     const void* q;            // [B, Hq, d]
     const void* k_pages;      // [num_pages, Hkv, page_size, d]
@@ -25,10 +29,10 @@ struct DecodeArgs {
     const int32_t* seq_lens;     // [B]
     void* out;                // [B, Hq, d]
     float* lse;               // [B, Hq] or nullptr
-    float* o_part;            // workspace [B, Hq, S, d]
-    float* lse_part;          // workspace [B, Hq, S]
+    float* o_part;            // workspace [slots, Hq / Hkv, d], slots = B * Hkv + kMaxStreamWaves
+    float* lse_part;          // workspace [slots, Hq / Hkv]
+    int* run_info;            // workspace [B * Hkv, 4]: each run's first slot, piece count, offset, share size
     int B, Hq, Hkv, d, page_size, W;
-    int num_splits;           // S
     int pages_per_split;
     float scale;
 };

@@ -189,20 +189,24 @@ int attn_kv_append(const void* k_new, const void* v_new, void* k_pages, void* v_
                    int max_pages_per_seq, attn_dtype_t dtype, hipStream_t stream);
 
 /*
- * Split plan of attn_decode_paged: the number of splits S each sequence's
- * page list is cut into (pages_per_split = ceil(max_pages_per_seq / S)).
- * num_splits > 0 asks for that many (clamped to max_pages_per_seq);
- * num_splits == 0 lets the library choose from the shape alone (no device
- * query, no device read).  Returns S >= 1, or a negative attn_status_t for
- * invalid sizes.
+ * Split plan of attn_decode_paged: a sequence's page list may be cut only at
+ * multiples of pages_per_split = ceil(max_pages_per_seq / S), so it is cut
+ * into at most S pieces; this returns S.  num_splits > 0 asks for that many
+ * (clamped to max_pages_per_seq); num_splits == 0 lets the library choose
+ * from the shape alone (no device query, no device read).  Returns S >= 1,
+ * or a negative attn_status_t for invalid sizes.
  */
 int attn_decode_num_splits(int B, int Hq, int Hkv, int d, int page_size,
                            int max_pages_per_seq, int num_splits);
 
 /*
- * Bytes of device workspace attn_decode_paged needs for this shape and split
- * request: fp32 partial outputs [B, Hq, S, d] and partial log-sum-exps
- * [B, Hq, S], each region 256-byte aligned.  Returns 0 for invalid sizes.
+ * Bytes of device workspace attn_decode_paged needs for this shape: with
+ * G = Hq / Hkv and P = B * Hkv + 4096 piece slots, fp32 partial outputs
+ * [P, G, d], fp32 partial log-sum-exps [P, G] and four int32 per
+ * (sequence, kv head), each region 256-byte aligned.  It grows with B, Hq
+ * and d only: the sequence lengths, max_pages_per_seq and the split request
+ * do not change it (the arguments are validated all the same).  Returns 0
+ * for invalid sizes.
  */
 size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int d, int page_size,
                                    int max_pages_per_seq, int num_splits);
@@ -225,7 +229,8 @@ size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int d, int page_size,
  *   num_splits     : as for attn_decode_num_splits (0 = automatic)
  *   workspace      : device, at least attn_decode_workspace_bytes(...) bytes;
  *                    owned by the caller, contents on entry are ignored
- *   dtype          : ATTN_BF16; d = 128 or 64; page_size = 16; Hq / Hkv <= 16
+ *   dtype          : ATTN_BF16; d = 128 or 64; page_size = 16; Hq / Hkv <= 16;
+ *                    B * Hkv * max_pages_per_seq < 2^31
  * Slots at or past seq_lens[b] may hold anything (NaN included): they are
  * never used.  The block table and seq_lens are read on the device only;
  * values outside the ranges above are undefined behaviour (check them with

@@ -280,12 +280,23 @@ def test_split_plan_and_workspace(lib):
     s4 = A.attn_decode_num_splits(32, 16, 8, 128, 16, 128, 0)
     s5 = A.attn_decode_num_splits(64, 32, 8, 128, 16, 512, 0)
     assert 32 * 8 * s4 >= 4096 and 64 * 8 * s5 >= 4096
-    for (B, Hq, Hkv, W, ns) in ((32, 16, 8, 128, 0), (64, 32, 8, 512, 0), (3, 6, 2, 9, 2)):
-        S = A.attn_decode_num_splits(B, Hq, Hkv, 128, 16, W, ns)
+    # Workspace: P = B * Hkv + 4096 piece slots of G = Hq / Hkv partial rows (d + 1 fp32 each, in two
+    # 256-byte aligned regions) plus a 16-byte record per (sequence, kv head); independent of W and the split.
+    def r256(x):
+        return (x + 255) // 256 * 256
+
+    for (B, Hq, Hkv, W, ns) in ((32, 16, 8, 128, 0), (64, 32, 8, 512, 0), (3, 6, 2, 9, 2), (4096, 32, 8, 8, 0)):
         need = A.attn_decode_workspace_bytes(B, Hq, Hkv, 128, 16, W, ns)
-        assert need >= B * Hq * S * (128 + 1) * 4
-        assert need % 256 == 0
+        rows = (B * Hkv + 4096) * (Hq // Hkv)
+        assert need == r256(rows * 128 * 4) + r256(rows * 4) + r256(B * Hkv * 16)
+        assert need == A.attn_decode_workspace_bytes(B, Hq, Hkv, 128, 16, 3 * W, 1)
+    assert A.attn_decode_workspace_bytes(64, 32, 8, 128, 16, 512, 0) < 10 * 2**20  # workload 5: under 10 MiB
     assert A.attn_decode_workspace_bytes(1, 3, 2, 128, 16, 4, 0) == 0  # invalid -> 0
+    # The flattened page stream is indexed with 32-bit offsets.
+    assert A.attn_decode_workspace_bytes(2**16, 8, 8, 128, 16, 2**12, 0) == 0
+    with pytest.raises(A.AttnError) as ei:
+        A.attn_decode_num_splits(2**16, 8, 8, 128, 16, 2**12, 0)
+    assert ei.value.status == A.ATTN_ERR_UNSUPPORTED
     with pytest.raises(A.AttnError):
         A.attn_decode_num_splits(1, 4, 2, 96, 16, 4, 0)
 

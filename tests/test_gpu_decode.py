@@ -52,14 +52,10 @@ def test_workload4_full():
     check(inp, synth.fp32_scale(shp.d), "workload 4 (B32 Hq16 Hkv8, L~U[32,2048], NaN-poisoned tails)")
 
 
-def test_workload5_decode_sampled():
+def test_workload5_decode_full():
     shp = synth.WORKLOADS[5]["decode"]
-    inp = synth.paged_inputs(shp, seed=105)
-    rng = np.random.default_rng(105)
-    L = inp.seq_lens.numpy()
-    batches = sorted(set([int(np.argmin(L)), int(np.argmax(L))] + [int(x) for x in rng.integers(0, shp.B, 6)]))
-    out, lse = check(inp, synth.fp32_scale(shp.d), "workload 5 decode (B64 Hq32 Hkv8, L~U[1024,8192])",
-                     batches=batches)
+    inp = synth.paged_inputs(shp, seed=105, poison=float("nan"))
+    out, lse = check(inp, synth.fp32_scale(shp.d), "workload 5 decode (B64 Hq32 Hkv8, L~U[1024,8192])")
     assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
 
 
@@ -211,3 +207,49 @@ def test_running_max_moves_across_pages(slope):
     inp.k_pages = kp.to(torch.bfloat16)
     for splits in (0, 1):
         check(inp, synth.fp32_scale(128), f"score ramp, slope {slope}, splits={splits}", num_splits=splits)
+
+
+# ------------------------------------------------------------------ batches past one sequence per lane
+def boundary_lens(B, seed):
+    """Lengths 0..900 with zero-length and one-token sequences on both sides of every multiple of 64 and of
+    the per-lane block size ceil(B / 64)."""
+    rng = np.random.default_rng(seed)
+    lens = rng.integers(2, 900, B)
+    per = (B + 63) // 64
+    for edge in sorted(set(range(64, B, 64)) | set(range(per, B, per))):
+        lens[edge - 1] = 0
+        lens[edge] = 1
+        if edge + 1 < B:
+            lens[edge + 1] = 0
+    lens[0] = 1
+    lens[-1] = 0
+    return [int(x) for x in lens]
+
+
+@pytest.mark.parametrize("B", [65, 130])
+@pytest.mark.parametrize("num_splits", [0, 3])
+def test_batches_past_64_sequences(B, num_splits):
+    """B > 64: each lane of the streaming kernel's scan sums a block of ceil(B / 64) sequences, and the
+    wave's share is found in two steps (block, then sequence).  Zero-length and one-token sequences sit at
+    the block and 64-sequence boundaries."""
+    lens = boundary_lens(B, seed=B + num_splits)
+    shp = synth.DecodeShape(B, 8, 2, 128, 16, 0, max(lens), torch.bfloat16)
+    inp = synth.paged_inputs(shp, seed=40 + B, seq_lens=lens, poison=float("nan"))
+    out, lse = check(inp, synth.fp32_scale(128), f"B={B} across lane blocks, splits={num_splits}",
+                     num_splits=num_splits)
+    zero = torch.tensor([L == 0 for L in lens])
+    assert torch.all(out[zero].float() == 0) and torch.all(torch.isneginf(lse[zero]))
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,lmax", [(1024, 8, 2, 512), (4096, 4, 1, 256)])
+def test_serving_batch_sizes(B, Hq, Hkv, lmax):
+    """Serving-size batches of short, ragged sequences (some empty), NaN in every unused slot; whole output
+    against the oracle, with the automatic plan and with two splits."""
+    rng = np.random.default_rng(B)
+    lens = rng.integers(1, lmax + 1, B)
+    lens[rng.random(B) < 0.05] = 0
+    lens = [int(x) for x in lens]
+    shp = synth.DecodeShape(B, Hq, Hkv, 128, 16, 0, lmax, torch.bfloat16)
+    inp = synth.paged_inputs(shp, seed=B + 1, seq_lens=lens, poison=float("nan"))
+    for ns in (0, 2):
+        check(inp, synth.fp32_scale(128), f"B={B} serving batch, splits={ns}", num_splits=ns)

@@ -145,41 +145,24 @@ def test_lse_is_optional_and_out_is_identical():
     assert l2 is None and torch.equal(o1.cpu(), o2.cpu())
 
 
-# ------------------------------------------------------------------ full-size workloads, sampled rows
-def sampled_rows(T, rng, n=24):
-    fixed = [0, 1, 63, 64, 65, 127, 128, T // 2, T - 65, T - 64, T - 2, T - 1]
-    rows = set(x for x in fixed if 0 <= x < T)
-    rows.update(int(x) for x in rng.integers(0, T, n))
-    return sorted(rows)
-
-
+# ------------------------------------------------------------------ full-size workloads, whole output
 @pytest.mark.parametrize("workload", [3, 5])
-def test_full_size_prefill_sampled(workload):
+def test_full_size_prefill_whole_output(workload):
+    """The benchmark's prefill workloads at full size, every element of out and lse against the oracle (one
+    oracle call per batch: 32 heads x T x T scores in fp64, about 0.5 s per head at T = 8192)."""
     shp = synth.WORKLOADS[workload]["prefill"]
     q, k, v = synth.prefill_inputs(shp, seed=workload)
     scale = synth.fp32_scale(shp.d)
     say(f"[prefill] workload {workload} full size {shp}")
     out, lse = run_prefill(q, k, v, scale)
     out, lse = out.cpu(), lse.cpu()
-    qn, kn, vn = q.float().numpy(), k.float().numpy(), v.float().numpy()  # exact upcast for the oracle
-    rng = np.random.default_rng(workload)
-    heads = sorted(set([0, shp.Hq - 1] + [int(x) for x in rng.integers(0, shp.Hq, 3)]))
     worst = 0.0
     for b in range(shp.B):
-        for h in heads:
-            rows = sampled_rows(shp.T, rng)
-            ro, rl = oracle.prefill_rows(qn, kn, vn, scale, b, h, rows)
-            worst = max(worst, max_err(np64(out[b, h, rows]), ro, f"w{workload} b{b} h{h} out", TOL_BF16))
-            max_err(np64(lse[b, h, rows]), rl, f"w{workload} b{b} h{h} lse", TOL_LSE)
-    say(f"    sampled max err {worst:.3e}")
-    # Properties at every position: finite; out is a convex combination of
-    # the kv head's values (|out| <= max |v|, up to one bf16 rounding); and
-    # lse_t >= s_t0, the score of key 0, which every row sees.
-    assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
-    vmax = v.float().abs().amax(dim=(2, 3)).repeat_interleave(shp.Hq // shp.Hkv, dim=1)
-    assert (out.float().abs().amax(dim=(2, 3)) <= vmax * (1 + 2.0**-8)).all()
-    s0 = scale * (q.float() * k.float()[:, :, :1].repeat_interleave(shp.Hq // shp.Hkv, dim=1)).sum(-1)
-    assert (lse >= s0 - 1e-3).all()
+        say(f"    oracle, batch {b}")
+        ro, rl = oracle.prefill(np64(q[b : b + 1]), np64(k[b : b + 1]), np64(v[b : b + 1]), scale)
+        worst = max(worst, max_err(np64(out[b : b + 1]), ro, f"w{workload} b{b} out", TOL_BF16))
+        max_err(np64(lse[b : b + 1]), rl, f"w{workload} b{b} lse", TOL_LSE)
+    say(f"    max err out {worst:.3e}")
 
 
 # ------------------------------------------------------------------ the lazy running-max rescale

@@ -57,3 +57,31 @@ def test_prefill_and_decode_on_two_streams_match_one_stream():
         torch.cuda.synchronize()
         for got, want in zip((out, lse, dout, dlse), ref):
             assert torch.equal(got, want)
+
+
+def test_decode_on_a_side_stream_without_workspace():
+    """workspace=None on a stream other than the current one: the binding allocates the workspace on the
+    launch stream, so memory the current stream allocates and overwrites right after the call (the same
+    size, freed and reused at once by torch's caching allocator if the two shared a pool) cannot be the
+    workspace the kernels are still using."""
+    dev = device()
+    dshape = synth.DecodeShape(64, 32, 8, 128, 16, 2000, 4000, torch.bfloat16)
+    inp = synth.paged_inputs(dshape, seed=43, poison=float("nan"))
+    dq, kp, vp, bt, sl = (t.to(dev) for t in (inp.q, inp.k_pages, inp.v_pages, inp.block_table, inp.seq_lens))
+    scale = synth.fp32_scale(128)
+    ref_o, ref_l = A.attn_decode_paged(dq, kp, vp, bt, sl, scale=scale)
+    torch.cuda.synchronize()
+    need = A.attn_decode_workspace_bytes(64, 32, 8, 128, 16, inp.max_pages_per_seq, 0)
+    side = torch.cuda.Stream()
+    main = torch.cuda.current_stream()
+    for r in range(4):
+        say(f"[streams] side-stream decode without workspace, round {r}")
+        out = torch.empty_like(dq)
+        lse = torch.empty(64, 32, dtype=torch.float32, device=dev)
+        side.wait_stream(main)
+        A.attn_decode_paged(dq, kp, vp, bt, sl, out=out, lse=lse, scale=scale, stream=side)
+        junk = torch.empty(need, dtype=torch.uint8, device=dev)  # on the current stream
+        junk.fill_(0xFF)
+        main.wait_stream(side)
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_o) and torch.equal(lse, ref_l)
