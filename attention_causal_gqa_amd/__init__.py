@@ -20,6 +20,7 @@ from ._binding import (  # noqa: F401
     attn_decode_num_splits,
     attn_decode_paged,
     attn_decode_paged_fp8,
+    attn_decode_paged_noalloc,
     attn_decode_workspace_bytes,
     attn_kv_append,
     attn_last_error_message,

@@ -51,6 +51,9 @@ def load_library():
     lib.attn_decode_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, i32, i32,
                                       vp, sz, vp]
     lib.attn_decode_paged.restype = i32
+    lib.attn_decode_paged_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32,
+                                              i32, i32, vp]
+    lib.attn_decode_paged_noalloc.restype = i32
     lib.attn_prefill_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, f32, i32,
                                        vp]
     lib.attn_prefill_paged.restype = i32
@@ -301,6 +304,35 @@ def attn_decode_paged(q, k_pages, v_pages, block_table, seq_lens, out=None, lse=
                                  None if lse is False else _ptr(lse), B, Hq, Hkv, d, page_size, P, W, float(scale),
                                  _dtype_code(q), num_splits, _ptr(workspace), ws_bytes, _stream(stream)))
     return out, (None if lse is False else lse)
+
+
+def attn_decode_paged_noalloc(q, k_pages, v_pages, block_table, seq_lens, out, lse=None, scale=None, num_splits=0,
+                              stream=None):
+    """attn_decode_paged without a workspace: the library's static per-GPU scratch serves instead, and nothing
+    is allocated (the caller passes out, and lse or None to skip it).  Calls overlapping on one GPU race."""
+    torch = _torch()
+    _require(q.dim() == 3 and k_pages.dim() == 4 and k_pages.shape == v_pages.shape, "bad q / page pool shapes")
+    B, Hq, d = q.shape
+    P, Hkv, page_size, dk = k_pages.shape
+    _require(dk == d, "page pools and q disagree on d")
+    _require(block_table.dim() == 2 and block_table.shape[0] == B and block_table.dtype == torch.int32,
+             "block_table must be int32 [B, W]")
+    _require(seq_lens.shape == (B,) and seq_lens.dtype == torch.int32, "seq_lens must be int32 [B]")
+    for n, t in (("q", q), ("k_pages", k_pages), ("v_pages", v_pages), ("block_table", block_table),
+                 ("seq_lens", seq_lens), ("out", out)):
+        _dense_on_gpu(n, t)
+    _require(q.dtype == k_pages.dtype == v_pages.dtype, "q and the page pools must share a dtype")
+    _require(out.shape == q.shape and out.dtype == q.dtype, "out must match q")
+    if lse is not None:
+        _dense_on_gpu("lse", lse)
+        _require(lse.shape == (B, Hq) and lse.dtype == torch.float32, "lse must be float32 [B, Hq]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    _check(load_library().attn_decode_paged_noalloc(_ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table),
+                                                    _ptr(seq_lens), _ptr(out), _ptr(lse), B, Hq, Hkv, d, page_size,
+                                                    P, block_table.shape[1], float(scale), _dtype_code(q),
+                                                    num_splits, _stream(stream)))
+    return out, lse
 
 
 def attn_decode_paged_fp8(q, k_pages, v_pages, k_scale, v_scale, block_table, seq_lens, out=None, lse=None,

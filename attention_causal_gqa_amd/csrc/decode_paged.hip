@@ -31,6 +31,7 @@
 // llm-from-scratch "Project Overview", "Performance Layer: kernel/ and
 // parallel/").
 #include <atomic>
+#include <mutex>
 #include <type_traits>
 
 #include "device_common.h"
@@ -703,7 +704,41 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream, float kscale, 
     return hipGetLastError();
 }
 
+// Workspace of attn_decode_paged_noalloc, for callers that cannot allocate:
+// device memory that each GPU the library runs on holds from the library's
+// load until the process ends.  Its host-side name is not a device address;
+// host code uses the address hipGetSymbolAddress returns for the device.
+static __device__ __align__(256) char scratch[kDecodeScratchBytes];
+
 }  // namespace
+
+hipError_t decode_scratch(hipStream_t stream, void** ptr) {
+    static std::mutex mu;
+    static void* addr[kMaxDevices];
+    hipDevice_t dev = 0;
+    hipError_t e = hipStreamGetDevice(stream, &dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (addr[dev] == nullptr) {
+        // Looked up once per device, with that device current: every GPU
+        // holds its own copy of the array at its own address.
+        int cur = 0;
+        if ((e = hipGetDevice(&cur)) != hipSuccess) return e;
+        if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (cur != dev) {
+            const hipError_t e2 = hipSetDevice(cur);
+            if (e == hipSuccess) e = e2;
+        }
+        if (e != hipSuccess) return e;
+        if (p == nullptr) return hipErrorInvalidSymbol;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
+}
 
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream) {
     return launch_decode<false>(a, stream, 1.0f, 1.0f);

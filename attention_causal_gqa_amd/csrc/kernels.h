@@ -62,4 +62,10 @@ hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_fp8(const DecodeArgs& a, float kscale, float vscale, hipStream_t stream);
 hipError_t launch_kv_append_bf16(const KvAppendArgs& a, hipStream_t stream);
 
+// Size of the decode scratch array (the workspace of the no-allocation
+// decode entry point), and its device address on the device that owns
+// `stream` (looked up once per device; no allocation).
+constexpr size_t kDecodeScratchBytes = (size_t)64 << 20;
+hipError_t decode_scratch(hipStream_t stream, void** ptr);
+
 }  // namespace attn

@@ -246,6 +246,30 @@ int attn_decode_paged(const void* q, const void* k_pages, const void* v_pages,
                       hipStream_t stream);
 
 /*
+ * attn_decode_paged without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Arguments, layouts and results are
+ * those of attn_decode_paged; the workspace is a static array of 64 MiB in
+ * the library's device code, one per GPU, held from the library's load until
+ * the process ends.  The call allocates and frees nothing.
+ *
+ * Limit: shapes whose attn_decode_workspace_bytes() exceeds 64 MiB (67108864
+ * bytes) are rejected with ATTN_ERR_WORKSPACE before any HIP call: about
+ * B * Hq * (d + 1) * 4 bytes plus 8.5 MB, so at Hq = 32, Hkv = 8, d = 128 up
+ * to B = 3524 sequences.  No part of the scratch needs to start at zero
+ * (every value a call reads, the call wrote first).
+ * Every call on a GPU uses that GPU's one array: calls that overlap in time
+ * on one GPU (on different streams, or from different threads) race and may
+ * return wrong results; serialise them.
+ */
+int attn_decode_paged_noalloc(const void* q, const void* k_pages, const void* v_pages,
+                              const int32_t* block_table, const int32_t* seq_lens,
+                              void* out, float* lse,
+                              int B, int Hq, int Hkv, int d, int page_size, int num_pages,
+                              int max_pages_per_seq, float scale, attn_dtype_t dtype,
+                              int num_splits, hipStream_t stream);
+
+/*
  * Single-token decode over a paged KV cache stored in FP8 E4M3.
  *
  *   k_pages,v_pages: device, [num_pages, Hkv, page_size, d] bytes, each an

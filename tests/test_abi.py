@@ -118,6 +118,42 @@ def test_decode_rejects(lib, kw, status):
     assert decode(lib, **kw) == status
 
 
+def decode_noalloc(lib, q=FAKE, kp=FAKE, vp=FAKE, bt=FAKE, sl=FAKE, out=FAKE, lse=None, B=2, Hq=4, Hkv=2, d=128,
+                   ps=16, P=10, W=8, scale=0.1, dtype=1, ns=0):
+    return lib.attn_decode_paged_noalloc(q, kp, vp, bt, sl, out, lse, B, Hq, Hkv, d, ps, P, W, scale, dtype, ns, None)
+
+
+@pytest.mark.parametrize(
+    "kw,status",
+    [
+        (dict(q=None), A.ATTN_ERR_INVALID_ARG),
+        (dict(out=None), A.ATTN_ERR_INVALID_ARG),
+        (dict(bt=FAKE + 2), A.ATTN_ERR_INVALID_ARG),
+        (dict(Hq=5, Hkv=2), A.ATTN_ERR_INVALID_ARG),
+        (dict(scale=float("inf")), A.ATTN_ERR_INVALID_ARG),
+        (dict(dtype=0), A.ATTN_ERR_UNSUPPORTED),
+        (dict(d=80), A.ATTN_ERR_UNSUPPORTED),
+        # 4000 sequences x 32 heads x (128 + 1) fp32 values, plus 4096 slots of 4 heads: past the 64 MiB scratch
+        (dict(B=4000, Hq=32, Hkv=8), A.ATTN_ERR_WORKSPACE),
+    ],
+)
+def test_decode_noalloc_rejects(lib, kw, status):
+    """The no-allocation decode checks every argument, and the workspace its shape needs against the 64 MiB
+    static scratch, before any HIP call."""
+    assert decode_noalloc(lib, **kw) == status
+    if status == A.ATTN_ERR_WORKSPACE:
+        msg = A.attn_last_error_message()
+        assert "67108864" in msg and str(lib.attn_decode_workspace_bytes(4000, 32, 8, 128, 16, 8, 0)) in msg
+
+
+def test_decode_noalloc_limit_is_the_workspace_size(lib):
+    # the largest batch of 32 heads (Hkv 8, d 128) that fits the scratch, and the next one
+    fits = [B for B in (3524, 3525) if lib.attn_decode_workspace_bytes(B, 32, 8, 128, 16, 8, 0) <= 64 << 20]
+    assert fits == [3524]
+    assert decode_noalloc(lib, B=3525, Hq=32, Hkv=8) == A.ATTN_ERR_WORKSPACE
+    assert decode_noalloc(lib, q=None, B=0) == A.ATTN_OK  # B = 0: nothing to do, nothing checked past the sizes
+
+
 def decode_fp8(lib, q=FAKE, kp=FAKE, vp=FAKE, ks=1.0, vs=1.0, bt=FAKE, sl=FAKE, out=FAKE, B=2, Hq=4, Hkv=2, d=128,
                ps=16, P=10, W=8, scale=0.1, ns=0, ws=FAKE, wsb=None):
     if wsb is None:
