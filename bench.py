@@ -12,15 +12,19 @@ synthetic tensors, resident in HBM before timing.
 Prints one JSON line.  ``value`` is the step's roofline fraction: the time the
 step's algorithmic work takes at MI355X peak (prefill flops at the bf16 MFMA
 peak plus decode bytes at the HBM peak) divided by the measured step time.
-``ms_per_step`` is host-clock time of K steps between two synchronizations.
-Per-kernel rates come from HIP events recorded on the launch stream around
-each part, in a second pass of K steps whose launches are queued while the
-GPU runs a short sleep kernel, so that the events time kernels rather than
-host launch latency.  A workload with a single part times its K queued
-launches between one pair of events instead, and in a two-part step the
-dominant kernel is also timed alone that way: ``roofline.achieved`` is its
-average launch duration.  ``ms_min``, ``ms_median`` and ``ms_p90`` of each
-part are always over the per-step event pairs.
+After the warm-up, untimed steps run until 30 have run in all (the GPU clock
+settles over the first few tens of steps).  The timed region is exactly K
+steps between two synchronizations: ``ms_per_step`` is their host-clock
+time, and ``kernel_ms_per_step`` with the median and p90 in ``step_events``
+comes from timing markers on the launch stream at each of those steps' ends.
+Per-part times come from a later pass of K steps with events around each
+part, queued behind a short GPU sleep so that the events time the kernels;
+in the two-stream step those events slow the step, so per-part times there
+are upper bounds.  A workload with a single part also times K queued
+launches between one pair of events, and in a two-part step the dominant
+kernel is timed alone that way: ``roofline.achieved`` is its average launch
+duration.  ``environment`` names the GPU, ROCm and torch, and the GFX clock
+amdsmi reports while the dominant kernel runs.
 
     python bench.py [--steps K] [--warmup W] [--workload 5|3|4|6|7|8|9] [--no-cpu-baseline] [--flush]
 
@@ -59,6 +63,79 @@ PEAK_BF16_FLOPS = 2.5e15  # MI355X dense bf16 MFMA, published
 PEAK_HBM_BYTES = 8.0e12   # MI355X HBM3E, published
 METRIC = "prefill TFLOP/s and paged-decode HBM GB/s, as fraction of MI355X peak"
 PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
+SETTLE_STEPS = 30  # untimed steps (warm-up included) before the timed region
+
+
+def environment():
+    """GPU, ROCm and torch versions of this run."""
+    props = torch.cuda.get_device_properties(0)
+    rocm = None
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            rocm = f.read().strip()
+    except OSError:
+        pass
+    return {"gpu": torch.cuda.get_device_name(0), "arch": getattr(props, "gcnArchName", None),
+            "compute_units": props.multi_processor_count, "rocm": rocm, "hip_runtime": torch.version.hip,
+            "torch": torch.__version__}
+
+
+def sample_gfx_clock(launch, seconds=1.5, skip=0.8):
+    """GFX clock (MHz) that amdsmi reports while `launch` runs back to back for `seconds`, or None when amdsmi is
+    not usable on this host.  The firmware's metrics table lags the GPU by about half a second (the reading stayed
+    at its idle value for ~0.5 s after a kernel loop started), so samples from the first `skip` seconds are
+    dropped.  Per-XCD current clocks when the table has them, else the single current clock."""
+    try:
+        import threading
+
+        import amdsmi
+
+        amdsmi.amdsmi_init()
+        handle = amdsmi.amdsmi_get_processor_handles()[0]
+        samples, done = [], threading.Event()
+        t_start = time.perf_counter()
+
+        def read():
+            try:
+                xcds = amdsmi.amdsmi_get_gpu_metrics_info(handle).get("current_gfxclks")
+                xcds = [float(c) for c in xcds if isinstance(c, (int, float)) and 0 < c < 65535]
+                if xcds:
+                    return xcds
+            except Exception:
+                pass
+            c = amdsmi.amdsmi_get_clock_info(handle, amdsmi.AmdSmiClkType.GFX)["clk"]
+            return [float(c)] if isinstance(c, (int, float)) and c > 0 else None
+
+        def poll():
+            while not done.is_set():
+                t = time.perf_counter() - t_start
+                try:
+                    v = read()
+                    if v is not None and t >= skip:
+                        samples.append(v)
+                except Exception:
+                    pass
+                time.sleep(0.01)
+
+        torch.cuda.synchronize()
+        th = threading.Thread(target=poll)
+        th.start()
+        while time.perf_counter() - t_start < seconds:
+            for _ in range(8):
+                launch()
+            torch.cuda.synchronize()
+        done.set()
+        th.join()
+        amdsmi.amdsmi_shut_down()
+        if not samples:
+            return None
+        means = [float(np.mean(v)) for v in samples]
+        return {"mhz_median": round(float(np.median(means)), 1), "mhz_min": round(float(min(means)), 1),
+                "per_xcd_last": samples[-1], "samples": len(samples),
+                "note": f"amdsmi current GFX clock (mean over XCDs) while the dominant kernel ran back to back; "
+                        f"samples after the first {skip} s of {seconds} s"}
+    except Exception:
+        return None
 
 
 def parse():
@@ -421,12 +498,13 @@ def main():
     start_ev = torch.cuda.Event()
     done_ev = {n: torch.cuda.Event() for n in names}
 
-    def step(events=None, seq=False):
-        """One step; events: {part: (start, end)} plus "step": (start, end), recorded if given."""
+    def step(events=None, seq=False, mark=None):
+        """One step.  events: {part: (start, end)}, recorded around each part on the stream it runs on;
+        mark: (start or None, end), recorded on the launch stream after the step's flush and at its end."""
         if flush_buf is not None:
             torch.sum(flush_buf, dim=0, out=flush_sink)
-        if events is not None:
-            events["step"][0].record(stream)
+        if mark is not None and mark[0] is not None:
+            mark[0].record(stream)
         if not concurrent or seq:
             for n in names:
                 if events is not None:
@@ -448,33 +526,62 @@ def main():
                 done_ev[n].record(ps)
             for n in order:
                 stream.wait_event(done_ev[n])
-        if events is not None:
-            events["step"][1].record(stream)
+        if mark is not None:
+            mark[1].record(stream)
+
+    def timing_event():
+        return torch.cuda.Event(enable_timing=True)
 
     def new_events():
-        return {n: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                for n in names + ["step"]}
+        return {n: (timing_event(), timing_event()) for n in names}
 
     for _ in range(args.warmup):
         step()
+    # Settling: the GPU's clock takes some tens of steps to settle after the
+    # process starts (the step's event span fell from 0.83-0.89 ms to 0.78 ms
+    # over the first ~25 steps of workload 5), so untimed steps are added
+    # until SETTLE_STEPS have run in all.
+    settle = max(0, SETTLE_STEPS - args.warmup)
+    for _ in range(settle):
+        step()
     torch.cuda.synchronize()
 
-    # Timed region B (per-kernel times): the same K steps with HIP events
-    # around each part, on the launch stream.  A GPU-side sleep first lets
-    # the host queue all K steps, so the events time the kernels and not the
-    # host's marshalling and launch latency (which exceeds a short decode).
-    # With two streams each part's events sit on its own stream, so a part's
-    # time is its duration inside the concurrent step.
+    # Timed region: exactly K steps between two synchronizations on the host
+    # clock.  The only events in it are one timing marker on the launch
+    # stream before the first step and one at the end of each step (with
+    # --flush, one more after each step's flush), so the per-step event times
+    # come from the same steps.  Events around the parts on their own streams
+    # are left out of it: they slowed the two-stream step of workload 5 by
+    # about 7% (0.720 against 0.671 ms on one box), the step-end markers by
+    # about 1%.
+    marks = [timing_event() for _ in range(args.steps + 1)]
+    starts = [timing_event() if flush_buf is not None else None for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    marks[0].record(stream)
+    for s in range(args.steps):
+        step(mark=(starts[s], marks[s + 1]))
+    issued = time.perf_counter() - t0
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_events = np.asarray([(starts[s] if flush_buf is not None else marks[s]).elapsed_time(marks[s + 1])
+                              for s in range(args.steps)])
+    step_ms = float(step_events.mean())
+
+    # Per-part times (diagnostic, after the timed region): K more steps with
+    # events around every part, queued behind a short GPU sleep so that the
+    # events time the kernels and not the host's launch latency.  In a
+    # two-stream step these events slow the step (see above): the per-part
+    # times inside it are upper bounds.
     evs = [new_events() for _ in range(args.steps)]
     torch.cuda.synchronize()
     torch.cuda._sleep(200_000 * args.steps)
     for s in range(args.steps):
         step(evs[s])
     torch.cuda.synchronize()
-
     per = {n: [evs[s][n][0].elapsed_time(evs[s][n][1]) for s in range(args.steps)] for n in names}
     ms = {n: float(np.mean(per[n])) for n in names}
-    step_ms = float(np.mean([evs[s]["step"][0].elapsed_time(evs[s]["step"][1]) for s in range(args.steps)]))
+
     ms_alone = None
     if concurrent:  # each part alone (one after the other), for reference
         evs2 = [new_events() for _ in range(args.steps)]
@@ -502,7 +609,7 @@ def main():
         torch.cuda.synchronize()
         dom_block_ms = e0.elapsed_time(e1) / args.steps
     if len(names) == 1 and flush_buf is None:
-        # One part per step: time the K queued launches between one pair of
+        # One part per step: also time K queued launches between one pair of
         # events, so that a short kernel's time does not carry the cost of an
         # event pair per launch (a few microseconds).  (With --flush the
         # per-step event pairs are kept: they leave out each step's flush.)
@@ -515,16 +622,6 @@ def main():
         e1.record(stream)
         torch.cuda.synchronize()
         ms[names[0]] = e0.elapsed_time(e1) / args.steps
-    # Timed region A (the step rate): K steps between two synchronizations,
-    # host clock.  It runs after the event passes, which leave the GPU in the
-    # steady state of a running loop (its clock takes some tens of steps to
-    # settle after the process starts).
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
     wall_seq = None
     if concurrent:  # the same K steps with the parts one after the other, for reference
         torch.cuda.synchronize()
@@ -533,12 +630,16 @@ def main():
             step(seq=True)
         torch.cuda.synchronize()
         wall_seq = time.perf_counter() - t0
+    # The shader clock while the dominant kernel runs back to back (sampled
+    # through amdsmi, when the host offers it).
+    dom_name = max(names, key=lambda n: ms[n])
+    sclk = sample_gfx_clock(work[dom_name])
 
-    kernel_ms = step_ms if len(names) > 1 else sum(ms.values())
+    kernel_ms = step_ms
     ms_per_step = wall * 1e3 / args.steps
 
     def spread(n):
-        """Min, median and 90th percentile of a part's per-step event times (timed region B)."""
+        """Min, median and 90th percentile of a part's per-step event times (the per-part pass)."""
         x = np.asarray(per[n])
         return {"ms_min": round(float(x.min()), 4), "ms_median": round(float(np.median(x)), 4),
                 "ms_p90": round(float(np.percentile(x, 90)), 4)}
@@ -666,8 +767,18 @@ def main():
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4),
         "kernel_ms_per_step": round(kernel_ms, 4),
+        "step_events": {"ms_median": round(float(np.median(step_events)), 4),
+                        "ms_p90": round(float(np.percentile(step_events, 90)), 4),
+                        "ms_min": round(float(step_events.min()), 4),
+                        "note": "timing markers on the launch stream at each of the K timed steps' ends (the steps "
+                                "of ms_per_step)"},
+        "settle_steps": settle,
+        "host_issue_ms_per_step": round(issued * 1e3 / args.steps, 4),
         **({"schedule": "decode and prefill on two HIP streams, joined once per step",
-            "ms_per_step_sequential": round(wall_seq * 1e3 / args.steps, 4)} if concurrent else {}),
+            "ms_per_step_sequential": round(wall_seq * 1e3 / args.steps, 4),
+            "parts_timing": "per-part events in a later pass of K two-stream steps (events on the part streams "
+                            "slow the step, so each part's ms is an upper bound); ms_alone: each part alone"}
+           if concurrent else {}),
         **({"flush": "512 MiB read before each step (outside the kernel events); value from kernel_ms_per_step"}
            if flush_buf is not None else {}),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
@@ -675,6 +786,7 @@ def main():
         "config": cfg,
         "parts": parts,
         "roofline": roof,
+        "environment": {**environment(), "gfx_clock_running_dominant": sclk},
     })
     if not args.no_cpu_baseline and args.workload == 5:
         result["cpu_baseline"] = cpu_baseline(pre_inputs, pre_shape, dec_inputs)
