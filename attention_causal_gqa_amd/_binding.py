@@ -13,7 +13,9 @@ import math
 import os
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libattn.so")
+# ATTN_LIBRARY names another build of the same library (for instance the
+# host-sanitized one that the CPU tests run the ABI checks against).
+LIB_PATH = os.environ.get("ATTN_LIBRARY") or os.path.join(PKG, "libattn.so")
 
 ATTN_OK = 0
 ATTN_ERR_INVALID_ARG = -1

@@ -170,9 +170,9 @@ const char* attn_status_string(int status) {
 const char* attn_last_error_message(void) { return g_last_error.c_str(); }
 
 int attn_prefill(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Hq, int Hkv, int T,
-                 int d, float scale, attn_dtype_t dtype, hipStream_t stream) {
+                 int d, float scale, int dtype, hipStream_t stream) {
     g_last_error.clear();
-    if (dtype != ATTN_F32 && dtype != ATTN_BF16) return fail(ATTN_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
+    if (dtype != ATTN_F32 && dtype != ATTN_BF16) return fail(ATTN_ERR_INVALID_ARG, "unknown dtype %d", dtype);
     if (B < 0 || T < 0) return fail(ATTN_ERR_INVALID_ARG, "B=%d, T=%d must be >= 0", B, T);
     if (Hq < 1 || Hkv < 1) return fail(ATTN_ERR_INVALID_ARG, "Hq=%d, Hkv=%d must be >= 1", Hq, Hkv);
     if (Hq % Hkv != 0) return fail(ATTN_ERR_INVALID_ARG, "Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
@@ -201,10 +201,10 @@ int attn_prefill(const void* q, const void* k, const void* v, void* out, float* 
 
 int attn_prefill_paged(const void* q, const void* k_pages, const void* v_pages, const int32_t* block_table,
                        const int32_t* seq_lens, void* out, float* lse, int B, int Hq, int Hkv, int Tq, int d,
-                       int page_size, int num_pages, int max_pages_per_seq, float scale, attn_dtype_t dtype,
+                       int page_size, int num_pages, int max_pages_per_seq, float scale, int dtype,
                        hipStream_t stream) {
     g_last_error.clear();
-    if (dtype != ATTN_F32 && dtype != ATTN_BF16) return fail(ATTN_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
+    if (dtype != ATTN_F32 && dtype != ATTN_BF16) return fail(ATTN_ERR_INVALID_ARG, "unknown dtype %d", dtype);
     if (B < 0 || Tq < 0) return fail(ATTN_ERR_INVALID_ARG, "B=%d, Tq=%d must be >= 0", B, Tq);
     if (Hq < 1 || Hkv < 1) return fail(ATTN_ERR_INVALID_ARG, "Hq=%d, Hkv=%d must be >= 1", Hq, Hkv);
     if (Hq % Hkv != 0) return fail(ATTN_ERR_INVALID_ARG, "Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
@@ -243,9 +243,9 @@ int attn_prefill_paged(const void* q, const void* k_pages, const void* v_pages, 
 
 int attn_prefill_varlen(const void* q, const void* k, const void* v, void* out, float* lse, const int32_t* cu_seqlens,
                         int num_seqs, int total_tokens, int max_seqlen, int Hq, int Hkv, int d, float scale,
-                        attn_dtype_t dtype, hipStream_t stream) {
+                        int dtype, hipStream_t stream) {
     g_last_error.clear();
-    if (dtype != ATTN_F32 && dtype != ATTN_BF16) return fail(ATTN_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
+    if (dtype != ATTN_F32 && dtype != ATTN_BF16) return fail(ATTN_ERR_INVALID_ARG, "unknown dtype %d", dtype);
     if (num_seqs < 0 || total_tokens < 0 || max_seqlen < 0)
         return fail(ATTN_ERR_INVALID_ARG, "num_seqs=%d, total_tokens=%d, max_seqlen=%d must be >= 0", num_seqs,
                     total_tokens, max_seqlen);
@@ -293,9 +293,9 @@ int attn_validate_varlen_metadata(const int32_t* cu_seqlens_host, int num_seqs, 
 
 int attn_kv_append(const void* k_new, const void* v_new, void* k_pages, void* v_pages, const int32_t* block_table,
                    const int32_t* seq_lens, int B, int Hkv, int Tn, int d, int page_size, int num_pages,
-                   int max_pages_per_seq, attn_dtype_t dtype, hipStream_t stream) {
+                   int max_pages_per_seq, int dtype, hipStream_t stream) {
     g_last_error.clear();
-    if (dtype != ATTN_F32 && dtype != ATTN_BF16) return fail(ATTN_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
+    if (dtype != ATTN_F32 && dtype != ATTN_BF16) return fail(ATTN_ERR_INVALID_ARG, "unknown dtype %d", dtype);
     if (B < 0 || Tn < 0) return fail(ATTN_ERR_INVALID_ARG, "B=%d, Tn=%d must be >= 0", B, Tn);
     if (Hkv < 1) return fail(ATTN_ERR_INVALID_ARG, "Hkv=%d must be >= 1", Hkv);
     if (d < 1) return fail(ATTN_ERR_INVALID_ARG, "d=%d must be >= 1", d);
@@ -335,10 +335,10 @@ size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int d, int page_size,
 
 int attn_decode_paged(const void* q, const void* k_pages, const void* v_pages, const int32_t* block_table,
                       const int32_t* seq_lens, void* out, float* lse, int B, int Hq, int Hkv, int d, int page_size,
-                      int num_pages, int max_pages_per_seq, float scale, attn_dtype_t dtype, int num_splits,
+                      int num_pages, int max_pages_per_seq, float scale, int dtype, int num_splits,
                       void* workspace, size_t workspace_bytes, hipStream_t stream) {
     g_last_error.clear();
-    if (dtype != ATTN_F32 && dtype != ATTN_BF16) return fail(ATTN_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
+    if (dtype != ATTN_F32 && dtype != ATTN_BF16) return fail(ATTN_ERR_INVALID_ARG, "unknown dtype %d", dtype);
     int st = check_decode_sizes(B, Hq, Hkv, d, page_size, max_pages_per_seq, num_splits);
     if (st != ATTN_OK) return st;
     if (num_pages < 0) return fail(ATTN_ERR_INVALID_ARG, "num_pages=%d must be >= 0", num_pages);
@@ -361,10 +361,10 @@ int attn_decode_paged(const void* q, const void* k_pages, const void* v_pages, c
 
 int attn_decode_paged_noalloc(const void* q, const void* k_pages, const void* v_pages, const int32_t* block_table,
                               const int32_t* seq_lens, void* out, float* lse, int B, int Hq, int Hkv, int d,
-                              int page_size, int num_pages, int max_pages_per_seq, float scale, attn_dtype_t dtype,
+                              int page_size, int num_pages, int max_pages_per_seq, float scale, int dtype,
                               int num_splits, hipStream_t stream) {
     g_last_error.clear();
-    if (dtype != ATTN_F32 && dtype != ATTN_BF16) return fail(ATTN_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
+    if (dtype != ATTN_F32 && dtype != ATTN_BF16) return fail(ATTN_ERR_INVALID_ARG, "unknown dtype %d", dtype);
     int st = check_decode_sizes(B, Hq, Hkv, d, page_size, max_pages_per_seq, num_splits);
     if (st != ATTN_OK) return st;
     if (num_pages < 0) return fail(ATTN_ERR_INVALID_ARG, "num_pages=%d must be >= 0", num_pages);

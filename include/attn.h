@@ -85,6 +85,9 @@ typedef enum attn_status {
     ATTN_ERR_HIP = -4          /* the HIP runtime reported an error while enqueuing */
 } attn_status_t;
 
+/* Element types.  Entry points take the value as a plain int `dtype`, so
+ * that any other value is a defined input (rejected with
+ * ATTN_ERR_INVALID_ARG) rather than an out-of-range enum. */
 typedef enum attn_dtype {
     ATTN_F32 = 0,  /* float32 q/k/v/out; fp32 arithmetic throughout */
     ATTN_BF16 = 1  /* bfloat16 q/k/v/out; fp32 accumulation, bf16 MFMA products */
@@ -106,7 +109,7 @@ typedef enum attn_dtype {
  */
 int attn_prefill(const void* q, const void* k, const void* v, void* out, float* lse,
                  int B, int Hq, int Hkv, int T, int d, float scale,
-                 attn_dtype_t dtype, hipStream_t stream);
+                 int dtype, hipStream_t stream);
 
 /*
  * Chunked causal prefill over a paged KV cache (see the file header).
@@ -134,7 +137,7 @@ int attn_prefill_paged(const void* q, const void* k_pages, const void* v_pages,
                        const int32_t* block_table, const int32_t* seq_lens,
                        void* out, float* lse,
                        int B, int Hq, int Hkv, int Tq, int d, int page_size, int num_pages,
-                       int max_pages_per_seq, float scale, attn_dtype_t dtype,
+                       int max_pages_per_seq, float scale, int dtype,
                        hipStream_t stream);
 
 /*
@@ -157,7 +160,7 @@ int attn_prefill_paged(const void* q, const void* k_pages, const void* v_pages,
  */
 int attn_prefill_varlen(const void* q, const void* k, const void* v, void* out, float* lse,
                         const int32_t* cu_seqlens, int num_seqs, int total_tokens, int max_seqlen,
-                        int Hq, int Hkv, int d, float scale, attn_dtype_t dtype, hipStream_t stream);
+                        int Hq, int Hkv, int d, float scale, int dtype, hipStream_t stream);
 
 /*
  * Host-side check of a host copy of cu_seqlens against the contract of
@@ -186,7 +189,7 @@ int attn_validate_varlen_metadata(const int32_t* cu_seqlens_host, int num_seqs, 
 int attn_kv_append(const void* k_new, const void* v_new, void* k_pages, void* v_pages,
                    const int32_t* block_table, const int32_t* seq_lens,
                    int B, int Hkv, int Tn, int d, int page_size, int num_pages,
-                   int max_pages_per_seq, attn_dtype_t dtype, hipStream_t stream);
+                   int max_pages_per_seq, int dtype, hipStream_t stream);
 
 /*
  * Split plan of attn_decode_paged: a sequence's page list may be cut only at
@@ -241,7 +244,7 @@ int attn_decode_paged(const void* q, const void* k_pages, const void* v_pages,
                       const int32_t* block_table, const int32_t* seq_lens,
                       void* out, float* lse,
                       int B, int Hq, int Hkv, int d, int page_size, int num_pages,
-                      int max_pages_per_seq, float scale, attn_dtype_t dtype,
+                      int max_pages_per_seq, float scale, int dtype,
                       int num_splits, void* workspace, size_t workspace_bytes,
                       hipStream_t stream);
 
@@ -266,7 +269,7 @@ int attn_decode_paged_noalloc(const void* q, const void* k_pages, const void* v_
                               const int32_t* block_table, const int32_t* seq_lens,
                               void* out, float* lse,
                               int B, int Hq, int Hkv, int d, int page_size, int num_pages,
-                              int max_pages_per_seq, float scale, attn_dtype_t dtype,
+                              int max_pages_per_seq, float scale, int dtype,
                               int num_splits, hipStream_t stream);
 
 /*

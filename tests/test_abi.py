@@ -364,7 +364,7 @@ def test_product_path_has_no_cpu_fallback():
 def test_asm_load_guard_flags_early_use():
     """The build-time ISA check: a register of an inline-asm load may be touched
     only after the vmcnt wait that retires that load."""
-    from attention_causal_gqa_amd.build import _asm_load_hazards
+    from attention_causal_gqa_amd.asm_guard import hazards as _asm_load_hazards
     head = "k:\n;;#ASMSTART\n\tglobal_load_dwordx4 v[50:53], v[34:35], off\n;;#ASMEND\n"
     assert _asm_load_hazards(head + "\tv_mov_b32_e32 v34, v50\n\ts_waitcnt vmcnt(0)\n")
     # loads retire in issue order: vmcnt(1) retires the older plain load, not the asm one
