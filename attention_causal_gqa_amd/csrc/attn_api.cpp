@@ -265,11 +265,12 @@ int attn_prefill_varlen(const void* q, const void* k, const void* v, void* out, 
     if (!aligned(cu_seqlens, 4) || (lse && !aligned(lse, 4)))
         return fail(ATTN_ERR_INVALID_ARG, "cu_seqlens and lse must be 4-byte aligned");
     const int64_t rows_per_block = 256 / (Hq / Hkv);
-    const int64_t blocks = (max_seqlen + rows_per_block - 1) / rows_per_block * num_seqs * Hkv;
+    const int64_t blocks = attn::varlen_items_bound(total_tokens, num_seqs, max_seqlen, rows_per_block) * Hkv;
     if (blocks > kMaxGrid) return fail(ATTN_ERR_INVALID_ARG, "problem too large: %lld workgroups", (long long)blocks);
 
     attn::PrefillArgs a{q, k, v, out, lse, num_seqs, Hq, Hkv, max_seqlen, d, scale};
-    return from_hip(attn::launch_prefill_varlen_bf16(a, cu_seqlens, stream), "attn_prefill_varlen launch");
+    return from_hip(attn::launch_prefill_varlen_bf16(a, cu_seqlens, total_tokens, stream),
+                    "attn_prefill_varlen launch");
 }
 
 int attn_validate_varlen_metadata(const int32_t* cu_seqlens_host, int num_seqs, int total_tokens, int max_seqlen) {

@@ -56,7 +56,16 @@ hipError_t launch_prefill_paged_bf16(const PrefillArgs& a, const int32_t* block_
 // Ragged batch packed along the token axis: a.q / a.out [N, Hq, d], a.k / a.v
 // [N, Hkv, d], a.lse [N, Hq]; a.B sequences, cu_seqlens [B+1]; a.T is the
 // longest sequence.
-hipError_t launch_prefill_varlen_bf16(const PrefillArgs& a, const int32_t* cu_seqlens, hipStream_t stream);
+// total_tokens = N.  The grid is Hkv * varlen_items_bound(...) workgroups.
+hipError_t launch_prefill_varlen_bf16(const PrefillArgs& a, const int32_t* cu_seqlens, int total_tokens,
+                                      hipStream_t stream);
+// Bound on the query blocks of BMt tokens over all S sequences of a packed
+// batch of N tokens, the longest Tmax: sum_s ceil(T_s / BMt) is at most
+// floor(N / BMt) + S and at most S * ceil(Tmax / BMt).
+inline int64_t varlen_items_bound(int64_t N, int64_t S, int64_t Tmax, int64_t BMt) {
+    const int64_t a = N / BMt + S, b = S * ((Tmax + BMt - 1) / BMt);
+    return a < b ? a : b;
+}
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream);
 // FP8 E4M3 page pools (one byte per value) with per-tensor scales.
 hipError_t launch_decode_fp8(const DecodeArgs& a, float kscale, float vscale, hipStream_t stream);

@@ -168,11 +168,70 @@ __global__ __launch_bounds__(512, 1) void prefill_bf16_kernel(const bf16* __rest
     const int l32 = lane & 31;
     const int hi = lane >> 5;
 
-    const int pairs = B * Hkv;
-    const int qb = nqb - 1 - (int)blockIdx.x / pairs;
-    const int pair = (int)blockIdx.x % pairs;
-    const int b = pair / Hkv;
-    const int kvh = pair % Hkv;
+    // Workgroup -> (sequence b, kv head kvh, query block qb).  Workgroup i
+    // runs on XCD i % 8 (the dispatcher deals workgroups to the 8 XCDs in
+    // turn, each XCD with its own L2).  The dense form takes the query blocks
+    // of every (sequence, kv head) pair level by level, last block first.
+    // The paged and packed forms, whose pairs read K/V slices larger than an
+    // L2, give each XCD its own pairs (when their count allows) and take a
+    // pair's query blocks one after another, last first, so that the
+    // workgroups reading one slice run close together on one L2.
+    const int bid = (int)blockIdx.x;
+    int b, kvh, qb;
+    if constexpr (kVarlen) {
+        // Item c of kv head kvh: query blocks of sequence 0 (last first), then
+        // of sequence 1, ...; sequence s has ceil(T_s / BMt) of them.  nqb is
+        // a bound on the items per kv head (the grid is Hkv * nqb).
+        int c;
+        if ((Hkv & 7) == 0) {
+            const int j = bid >> 3, hpx = Hkv >> 3;
+            kvh = (bid & 7) + 8 * (j % hpx);
+            c = j / hpx;
+        } else {
+            kvh = bid % Hkv;
+            c = bid / Hkv;
+        }
+        // Find the sequence whose items hold c: a scan of the item counts,
+        // 64 sequences at a time (every wave does the same, uniformly).
+        const int ln = threadIdx.x & 63;
+        int found = -1, first = 0, count = 0, base = 0;
+        for (int s0 = 0; s0 < B; s0 += 64) {
+            const int sq = s0 + ln;
+            const int n = sq < B ? (seq_lens[sq + 1] - seq_lens[sq] + BMt - 1) / BMt : 0;
+            int inc = n;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const int y = __shfl_up(inc, o);
+                if (ln >= o) inc += y;
+            }
+            const int ex = base + inc - n;
+            const unsigned long long hit = __ballot(n > 0 && c >= ex && c < ex + n);
+            if (hit) {
+                const int l = __ffsll((long long)hit) - 1;
+                found = s0 + l;
+                first = __shfl(ex, l);
+                count = __shfl(n, l);
+                break;
+            }
+            base += __shfl(inc, 63);
+        }
+        if (found < 0) return;  // past the last item: the whole workgroup, before any barrier
+        b = __builtin_amdgcn_readfirstlane(found);
+        qb = __builtin_amdgcn_readfirstlane(count - 1 - (c - first));
+    } else {
+        const int pairs = B * Hkv;
+        int pair;
+        if (kPaged && (pairs & 7) == 0) {
+            const int j = bid >> 3;
+            pair = (bid & 7) + 8 * (j / nqb);
+            qb = nqb - 1 - j % nqb;
+        } else {
+            pair = bid % pairs;
+            qb = nqb - 1 - bid / pairs;
+        }
+        b = pair / Hkv;
+        kvh = pair % Hkv;
+    }
     const int t0 = qb * BMt;
     // Queries of this sequence (Tb), the position of query 0 (pos0), and in
     // the packed form the sequence's first token (tok0).
@@ -182,7 +241,7 @@ __global__ __launch_bounds__(512, 1) void prefill_bf16_kernel(const bf16* __rest
     if constexpr (kVarlen) {
         tok0 = (size_t)seq_lens[b];
         Tb = seq_lens[b + 1] - seq_lens[b];
-        if (t0 >= Tb) return;  // the whole workgroup, before any barrier
+        if (t0 >= Tb) return;  // never taken (qb < ceil(Tb / BMt)); before any barrier
     }
     const int kend = pos0 + min(t0 + BMt, Tb);  // keys 0..kend-1 are visible to some row
 
@@ -500,11 +559,15 @@ __global__ __launch_bounds__(512, 1) void prefill_bf16_kernel(const bf16* __rest
 }
 
 template <int D, int kMode>
-hipError_t launch_d(const PrefillArgs& a, const int* block_table, const int* seq_lens, int W, hipStream_t stream) {
+hipError_t launch_d(const PrefillArgs& a, const int* block_table, const int* seq_lens, int W, hipStream_t stream,
+                    int total_tokens = 0) {
     const int G = a.Hq / a.Hkv;
     const int BMt = kRows / G;
-    const int nqb = (a.T + BMt - 1) / BMt;
-    const dim3 grid((unsigned)nqb * a.B * a.Hkv);
+    // Query blocks per (sequence, kv head) pair; in the packed form, a bound
+    // on the blocks of all sequences: sum ceil(T_s / BMt) <= N / BMt + S.
+    const int nqb = kMode == kVarlenMode ? (int)varlen_items_bound(total_tokens, a.B, a.T, BMt)
+                                         : (a.T + BMt - 1) / BMt;
+    const dim3 grid(kMode == kVarlenMode ? (unsigned)nqb * a.Hkv : (unsigned)nqb * a.B * a.Hkv);
     const float c1 = (float)((double)a.scale * 1.4426950408889634);
     if (c1 > 0.f) {
         hipLaunchKernelGGL((prefill_bf16_kernel<D, true, kMode>), grid, dim3(512), 0, stream, (const bf16*)a.q,
@@ -531,9 +594,10 @@ hipError_t launch_prefill_paged_bf16(const PrefillArgs& a, const int32_t* block_
                       : launch_d<64, kPagedMode>(a, block_table, seq_lens, W, stream);
 }
 
-hipError_t launch_prefill_varlen_bf16(const PrefillArgs& a, const int32_t* cu_seqlens, hipStream_t stream) {
-    return a.d == 128 ? launch_d<128, kVarlenMode>(a, nullptr, cu_seqlens, 0, stream)
-                      : launch_d<64, kVarlenMode>(a, nullptr, cu_seqlens, 0, stream);
+hipError_t launch_prefill_varlen_bf16(const PrefillArgs& a, const int32_t* cu_seqlens, int total_tokens,
+                                      hipStream_t stream) {
+    return a.d == 128 ? launch_d<128, kVarlenMode>(a, nullptr, cu_seqlens, 0, stream, total_tokens)
+                      : launch_d<64, kVarlenMode>(a, nullptr, cu_seqlens, 0, stream, total_tokens);
 }
 
 }  // namespace attn
