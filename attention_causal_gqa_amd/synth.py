@@ -136,6 +136,9 @@ WORKLOADS[8] = {"varlen": VarlenShape(16, 32, 8, 128, 256, 4096, torch.bfloat16)
 # Paged decode over an FP8 E4M3 cache (seed 109): workload 5's decode shape.
 WORKLOADS[9] = {"decode_fp8": DecodeShape(64, 32, 8, 128, PAGE_SIZE, 1024, 8192, torch.bfloat16)}
 
+# A serving-size decode batch (seed 110): 1024 short ragged sequences, K/V (1.1 GB) far larger than the MALL.
+WORKLOADS[10] = {"decode": DecodeShape(1024, 32, 8, 128, PAGE_SIZE, 16, 512, torch.bfloat16)}
+
 WORKLOAD_NAMES = {
     1: "causal MHA prefill fp32 B1 H4 T128 d64",
     2: "causal GQA prefill bf16 B1 Hq16 Hkv8 T512 d128",
@@ -146,6 +149,7 @@ WORKLOAD_NAMES = {
     7: "KV append bf16 into a paged cache B4 Hkv8 Tn2048 d128 page16 L~U[4096,16384]",
     8: "ragged prefill bf16 over packed tokens S16 Hq32 Hkv8 d128 T~U[256,4096]",
     9: "paged decode over an FP8 E4M3 cache B64 Hq32 Hkv8 d128 page16 L~U[1024,8192]",
+    10: "paged decode bf16 serving batch B1024 Hq32 Hkv8 d128 page16 L~U[16,512]",
 }
 
 

@@ -26,7 +26,7 @@ kernel is timed alone that way: ``roofline.achieved`` is its average launch
 duration.  ``environment`` names the GPU, ROCm and torch, and the GFX clock
 amdsmi reports while the dominant kernel runs.
 
-    python bench.py [--steps K] [--warmup W] [--workload 5|3|4|6|7|8|9] [--no-cpu-baseline] [--flush]
+    python bench.py [--steps K] [--warmup W] [--workload 5|3|4|6|7|8|9|10] [--no-cpu-baseline] [--flush]
 
 ``--flush`` reads a 512 MiB buffer before every step (outside the events),
 so that a decode whose K/V would fit in the 256 MB MALL (workload 4) starts
@@ -38,8 +38,10 @@ Workload 7 times the KV append that writes such chunks into the cache.
 Workload 8 times the ragged prefill of 16 sequences of 256..4096 tokens
 packed along the token axis.  Workload 9 times the paged decode of workload
 5 over an FP8 E4M3 cache (algorithmic bytes: one byte per cached value).
+Workload 10 times a serving-size decode batch: 1024 sequences of 16..512
+tokens (Hq32 Hkv8 d128).
     python bench.py --copy-calibration   # plain 1 GiB copy, reference for HBM byte counters
-    python bench.py --read-ceiling       # plain reads: 2 GiB, and workload 5's decode slices
+    python bench.py --read-ceiling       # plain reads: 2 GiB, and the decode slices of workloads 5 and 9
 """
 
 import argparse
@@ -143,7 +145,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workload", type=int, default=5, choices=(3, 4, 5, 6, 7, 8, 9))
+    p.add_argument("--workload", type=int, default=5, choices=(3, 4, 5, 6, 7, 8, 9, 10))
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--sequential", action="store_true",
                    help="run the parts of a two-part step (workload 5) one after the other on one stream; by default "
@@ -175,9 +177,10 @@ def copy_calibration():
 
 def read_ceiling(args):
     """The practical HBM read ceiling: a kernel that only reads (libattn_probe.so), timed with HIP events
-    over K launches, on (1) a 2 GiB buffer in 4 KiB slices and (2) the 4 KiB K and V slices of workload
-    5's decode pool, (sequence, kv head, page) in the streaming decode's order, from a pool far larger
-    than the MALL.  Context for the decode's rate, not a replacement for the 8 TB/s peak."""
+    over K launches, on (1) a 2 GiB buffer in 4 KiB slices, (2) the 4 KiB K and V slices of workload 5's
+    decode pool and (3) the 2 KiB K and V slices of workload 9's FP8 pool, (sequence, kv head, page) in the
+    streaming decode's order, from pools far larger than the MALL.  Context for the decode's rate, not a
+    replacement for the 8 TB/s peak."""
     import ctypes
     lib = ctypes.CDLL(os.path.join(ROOT, "attention_causal_gqa_amd", "libattn_probe.so"))
     vp = ctypes.c_void_p
@@ -187,9 +190,8 @@ def read_ceiling(args):
     blocks = torch.cuda.get_device_properties(dev).multi_processor_count * 8
     sink = torch.zeros(256, dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream()
-    slice_bytes = 4096
 
-    def timed(base, offs, n):
+    def timed(base, offs, n, slice_bytes):
         def go():
             rc = lib.probe_read_slices(base.data_ptr(), None if offs is None else offs.data_ptr(), n, slice_bytes,
                                        sink.data_ptr(), blocks, ctypes.c_void_p(stream.cuda_stream))
@@ -205,29 +207,41 @@ def read_ceiling(args):
         e1.record(stream)
         torch.cuda.synchronize()
         ms = e0.elapsed_time(e1) / args.steps
-        return ms, n * slice_bytes / (ms / 1e3) / 1e9
+        return {"slices": int(n), "slice_bytes": slice_bytes, "bytes": int(n) * slice_bytes, "ms": round(ms, 4),
+                "gbps": round(n * slice_bytes / (ms / 1e3) / 1e9, 1)}
 
+    def decode_slices(seq_lens, block_table, P, Hkv, page_size, slice_bytes):
+        """Byte offsets of the K and V slices one decode reads, in its order, in a K pool then V pool."""
+        offs = []
+        for b in range(seq_lens.shape[0]):
+            n = (int(seq_lens[b]) + page_size - 1) // page_size
+            pages = block_table[b, :n].long()
+            for kvh in range(Hkv):
+                ko = (pages * Hkv + kvh) * slice_bytes
+                offs.append(torch.stack([ko, ko + P * Hkv * slice_bytes], dim=1).reshape(-1))
+        return torch.cat(offs).to(dev)
+
+    out = {}
     big = torch.ones(2 << 30, dtype=torch.uint8, device=dev)
-    c_ms, c_gbps = timed(big, None, big.numel() // slice_bytes)
+    out["contiguous"] = timed(big, None, big.numel() // 4096, 4096)
     del big
     shp = synth.WORKLOADS[5]["decode"]
     inp = synth.paged_inputs(shp, seed=105)
-    P, Hkv = inp.k_pages.shape[0], shp.Hkv
-    pool = torch.ones(2 * P * Hkv * slice_bytes, dtype=torch.uint8, device=dev)  # K pool, then V pool
-    offs = []
-    for b in range(shp.B):
-        n = (int(inp.seq_lens[b]) + shp.page_size - 1) // shp.page_size
-        pages = inp.block_table[b, :n].long()
-        for kvh in range(Hkv):
-            ko = (pages * Hkv + kvh) * slice_bytes
-            offs.append(torch.stack([ko, ko + P * Hkv * slice_bytes], dim=1).reshape(-1))
-    offs = torch.cat(offs).to(dev)
-    p_ms, p_gbps = timed(pool, offs, offs.numel())
-    print(json.dumps({"read_ceiling": {
-        "contiguous": {"bytes": 2 << 30, "ms": round(c_ms, 4), "gbps": round(c_gbps, 1)},
-        "decode_pages_w5": {"slices": int(offs.numel()), "bytes": int(offs.numel()) * slice_bytes, "ms": round(p_ms, 4),
-                            "gbps": round(p_gbps, 1)},
-        "blocks": blocks, "slice_bytes": slice_bytes, "steps": args.steps}}), flush=True)
+    P = inp.k_pages.shape[0]
+    sb = shp.page_size * shp.d * 2
+    pool = torch.ones(2 * P * shp.Hkv * sb, dtype=torch.uint8, device=dev)  # K pool, then V pool
+    offs = decode_slices(inp.seq_lens, inp.block_table, P, shp.Hkv, shp.page_size, sb)
+    out["decode_pages_w5"] = timed(pool, offs, offs.numel(), sb)
+    del pool, inp
+    shp = synth.WORKLOADS[9]["decode_fp8"]
+    inp = synth.fp8_paged_inputs(shp, seed=109)
+    P = inp.k_codes.shape[0]
+    sb = shp.page_size * shp.d
+    pool = torch.ones(2 * P * shp.Hkv * sb, dtype=torch.uint8, device=dev)
+    offs = decode_slices(inp.seq_lens, inp.block_table, P, shp.Hkv, shp.page_size, sb)
+    out["decode_pages_w9_fp8"] = timed(pool, offs, offs.numel(), sb)
+    out.update({"blocks": blocks, "steps": args.steps})
+    print(json.dumps({"read_ceiling": out}), flush=True)
 
 
 def kernel_source_hash(names):

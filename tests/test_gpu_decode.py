@@ -59,6 +59,13 @@ def test_workload5_decode_full():
     assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
 
 
+def test_workload10_serving_batch_full():
+    shp = synth.WORKLOADS[10]["decode"]
+    inp = synth.paged_inputs(shp, seed=110, poison=float("nan"))
+    out, lse = check(inp, synth.fp32_scale(shp.d), "workload 10 (B1024 Hq32 Hkv8, L~U[16,512], NaN-poisoned tails)")
+    assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
+
+
 # ------------------------------------------------------------------ lengths at page and split edges
 EDGE_LENS = [1, 2, 15, 16, 17, 31, 32, 33, 63, 64, 65, 255, 256, 257, 1000, 2047, 2048]
 
