@@ -152,6 +152,10 @@ def parse():
                         "the decode and the prefill run on two HIP streams, joined once per step")
     p.add_argument("--flush", action="store_true",
                    help="read a 512 MiB buffer before each step (outside the kernel events) to evict L2/MALL")
+    p.add_argument("--no-clock", action="store_true",
+                   help="skip the GFX clock sample (1.5 s of the dominant kernel back to back after the timed region); "
+                        "the kernel-trace profiles use it so that their per-kernel averages cover the benchmark's "
+                        "own launches only")
     p.add_argument("--read-ceiling", action="store_true",
                    help="only time plain reads: a 2 GiB buffer, and workload 5's K/V page slices in decode order")
     p.add_argument("--copy-calibration", action="store_true",
@@ -647,7 +651,7 @@ def main():
     # The shader clock while the dominant kernel runs back to back (sampled
     # through amdsmi, when the host offers it).
     dom_name = max(names, key=lambda n: ms[n])
-    sclk = sample_gfx_clock(work[dom_name])
+    sclk = None if args.no_clock else sample_gfx_clock(work[dom_name])
 
     kernel_ms = step_ms
     ms_per_step = wall * 1e3 / args.steps
