@@ -278,12 +278,15 @@ __global__ __launch_bounds__(512, 1) void prefill_bf16_kernel(const bf16* __rest
     constexpr int NDW = 2 * NIW;
     int drow[NDW];
     uint32_t doff[NDW];  // byte offset of the lane's chunk within a tile of rows
+    uint32_t poff[NDW];  // paged form: byte offset of the lane's chunk within its (page, kv head) slice
     int dslot[NDW];      // wave-wide DMA index within the tile
+    static_assert(kPage % RPI == 0, "a wave-wide DMA's rows must lie in one page");
 #pragma unroll
     for (int j = 0; j < NDW; ++j) {
         dslot[j] = ((w & 3) + 4 * (j / NIW)) * NIW + j % NIW;
         drow[j] = RPI * dslot[j] + lane / CPR;
         doff[j] = (uint32_t)(drow[j] * krs + 16 * ((lane % CPR) ^ swz<CPR>(drow[j])));
+        poff[j] = (uint32_t)((drow[j] % kPage) * ROWB + 16 * ((lane % CPR) ^ swz<CPR>(drow[j])));
     }
     // Keys at or past kend (the paged form) or Tb (the dense and packed
     // forms) are read as the last one before it: they are masked for every
@@ -294,12 +297,23 @@ __global__ __launch_bounds__(512, 1) void prefill_bf16_kernel(const bf16* __rest
         if constexpr (kPaged) {
             // (page, kv head) slices are kPage rows of ROWB bytes, Hkv slices per page.
             const char* bb = reinterpret_cast<const char*>(base);
+            if (k0 + kBN <= kend) {
+                // A whole tile: the RPI rows of one wave-wide DMA lie in one
+                // page, so its page id is wave-uniform and the slice address
+                // is scalar work; each lane adds its fixed offset in the slice.
 #pragma unroll
-            for (int j = 0; j < NDW; ++j) {
-                const int key = min(k0 + drow[j], kend - 1);
-                const size_t page = (size_t)bt_lds[key / kPage];
-                dma16(bb + (page * Hkv * kPage + key % kPage) * ROWB + (doff[j] - (uint32_t)(drow[j] * ROWB)),
-                      dst + 1024 * dslot[j]);
+                for (int j = 0; j < NDW; ++j) {
+                    const int pg = __builtin_amdgcn_readfirstlane(bt_lds[(k0 + RPI * dslot[j]) / kPage]);
+                    dma16(bb + (size_t)pg * (size_t)(Hkv * kPage * ROWB) + poff[j], dst + 1024 * dslot[j]);
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < NDW; ++j) {
+                    const int key = min(k0 + drow[j], kend - 1);
+                    const size_t page = (size_t)bt_lds[key / kPage];
+                    dma16(bb + (page * Hkv * kPage + key % kPage) * ROWB + (doff[j] - (uint32_t)(drow[j] * ROWB)),
+                          dst + 1024 * dslot[j]);
+                }
             }
         } else if (k0 + kBN <= Tb) {
             const char* tb = reinterpret_cast<const char*>(base) + (size_t)k0 * krs;
