@@ -49,7 +49,9 @@ def check(inp, scale, what, rows=None, batches=None):
 
 
 @pytest.mark.parametrize("Hq,Hkv,d", [(8, 2, 128), (4, 4, 128), (16, 2, 128), (32, 4, 128), (8, 1, 128),
-                                      (8, 2, 64), (6, 3, 64)])
+                                      (8, 2, 64), (6, 3, 64),
+                                      # B * Hkv a multiple of 8: the per-XCD pair order
+                                      (8, 8, 128), (16, 8, 64)])
 def test_chunk_parity_group_sizes(Hq, Hkv, d):
     shp = synth.ChunkShape(3, Hq, Hkv, 100, d, synth.PAGE_SIZE, 100, 700, BF16)
     inp = synth.chunk_inputs(shp, seed=600 + Hq + Hkv + d, poison=float("nan"))

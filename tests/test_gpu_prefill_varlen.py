@@ -28,6 +28,8 @@ def run_varlen(q, k, v, cu, max_seqlen, scale):
     (32, 4, 128, [257, 31]),
     (8, 1, 64, [90, 1, 180]),
     (6, 3, 64, [65, 64, 63]),
+    (8, 8, 128, [70, 300, 1]),        # Hkv a multiple of 8: each XCD serves its own kv head
+    (16, 16, 64, [100, 1, 257, 64]),  # two kv heads per XCD
 ])
 def test_varlen_parity(Hq, Hkv, d, lens):
     shp = synth.VarlenShape(len(lens), Hq, Hkv, d, 1, max(lens), BF16)
