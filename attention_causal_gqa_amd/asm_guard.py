@@ -241,7 +241,8 @@ def writes(op, ops):
 
 
 # ---- symbolic scalar state ------------------------------------------------
-# A literal is True (always), False (never) or (atom, polarity).  A lane mask
+# A literal is True (always), False (never), (atom, polarity), ("and", l1, l2)
+# (both hold; at most four atoms) or ("not", l) (l fails).  A lane mask
 # is ("zero",), ("uni", lit, E) = lit ? lanes of E : none, ("nuni", lit, E) =
 # its complement, or absent (unknown).  E is an exec token: "ALL" (every
 # lane), ("e0",) (the lanes the wave started with), or a token from an exec
@@ -251,7 +252,23 @@ def writes(op, ops):
 def _neg(lit):
     if lit is True or lit is False:
         return not lit
+    if lit[0] == "not":
+        return lit[1]
+    if lit[0] == "and":
+        return ("not", lit)
     return (lit[0], not lit[1])
+
+
+def _conj(a, b):
+    """The literal a and b (conjunctions of at most four comparisons; None beyond)."""
+    if a is False or b is False:
+        return False
+    if a is True:
+        return b
+    if b is True or a == b:
+        return a
+    lit = ("and", a, b)
+    return lit if len(_atoms_in(lit, set())) <= 4 else None
 
 
 class _State:
@@ -322,10 +339,36 @@ class _Analysis:
         return False
 
     def truth(self, st, lit):
+        """True, False or None (unknown) for a literal on the path whose facts are st.facts."""
         if lit is True or lit is False:
             return lit
+        if lit[0] == "not":
+            t = self.truth(st, lit[1])
+            return None if t is None else not t
+        if lit[0] == "and":
+            ta, tb = self.truth(st, lit[1]), self.truth(st, lit[2])
+            if ta is False or tb is False:
+                return False
+            return True if (ta is True and tb is True) else None
         v = st.facts.get(lit[0])
         return None if v is None else v == lit[1]
+
+    def learn(self, st, lit, val):
+        """Record on st what `lit` having truth `val` implies about single comparisons."""
+        if lit is True or lit is False:
+            return
+        if lit[0] == "not":
+            self.learn(st, lit[1], not val)
+        elif lit[0] == "and":
+            if val:
+                self.learn(st, lit[1], True)
+                self.learn(st, lit[2], True)
+            elif self.truth(st, lit[1]) is True:
+                self.learn(st, lit[2], False)
+            elif self.truth(st, lit[2]) is True:
+                self.learn(st, lit[1], False)
+        elif st.facts.get(lit[0]) is None:
+            st.facts[lit[0]] = lit[1] == val
 
     # operand values
     def value_id(self, st, tok):
@@ -382,11 +425,10 @@ class _Analysis:
                 inner, outer = b, a
             else:
                 return None
-            if outer[1] is True:
-                return ("uni", inner[1], inner[2])
-            if inner[1] is True or inner[1] == outer[1]:
-                return ("uni", outer[1], inner[2])
-            return None
+            lit = _conj(inner[1], outer[1])
+            if lit is None:
+                return ("sub", inner[2])
+            return ("zero",) if lit is False else ("uni", lit, inner[2])
         if a[0] == "uni" and b[0] == "nuni":
             # lanes(Ea) if la, minus (lanes(Eb) if lb)
             if a[1] is True and self.subset(a[2], b[2]):
@@ -592,8 +634,8 @@ class _Analysis:
                 if t is not None and t != val:
                     return
             s2 = st.copy()
-            if lit is not None and lit not in (True, False) and self.truth(st, lit) is None:
-                s2.facts[lit[0]] = lit[1] == val
+            if lit is not None and self.truth(st, lit) is None:
+                self.learn(s2, lit, val)
             if extra_nonempty is not None:
                 s2.nonempty = s2.nonempty | {extra_nonempty}
             out.append((j, s2))
@@ -642,7 +684,14 @@ def _merge(an, a, b, j):
         if v is not None and v != ("sub", "ALL"):
             m.masks[d] = v
     m.scc = a.scc if a.scc == b.scc else None
-    m.vuni = {r: v for r, v in a.vuni.items() if b.vuni.get(r) == v}
+    m.vuni = {}
+    for r in set(a.vuni) & set(b.vuni):
+        va, vb = a.vuni[r], b.vuni[r]
+        if va == vb:
+            m.vuni[r] = va
+        elif va[1:] == vb[1:] and _current(a, va[0]) is not None and _current(a, va[0]) == _current(b, vb[0]):
+            # on both paths the register holds the current value of the same scalar registers
+            m.vuni[r] = (("s",) + tuple((x, m.version(x)) for x in _current(a, va[0])),) + va[1:]
     m.vbool = {r: v for r, v in a.vbool.items() if b.vbool.get(r) == v}
     if a.exec == b.exec:
         m.exec = a.exec
@@ -660,18 +709,31 @@ def _merge(an, a, b, j):
     return m
 
 
+def _current(st, vid):
+    """The scalar registers whose present values a value id names, or None."""
+    if vid[0] != "s" or any(st.version(r) != v for r, v in vid[1:]):
+        return None
+    return tuple(r for r, _ in vid[1:])
+
+
 def _same(a, b):
     return (a.pending == b.pending and a.ver == b.ver and a.epoch == b.epoch and a.masks == b.masks
             and a.scc == b.scc and a.vuni == b.vuni and a.vbool == b.vbool and a.exec == b.exec
             and a.nonempty == b.nonempty)
 
 
-def _defined_in(obj, body):
-    """Whether a fact, mask or value (nested tuples) names a version or exec token made inside `body`."""
+def _defined_in(obj, body, hdr=None):
+    """Whether a fact, mask or value (nested tuples) names a version or exec token made inside `body`.
+    With hdr = (j, W), a join inside the loop of a register outside W (those the loop never writes) counts
+    as made before the loop: whichever path reached the join, the register still holds its value from the
+    loop's entry, so every iteration of one run of the loop sees that same value."""
     if isinstance(obj, tuple):
         if len(obj) >= 2 and obj[0] in ("d", "phi", "hdr", "x", "many") and isinstance(obj[1], int):
+            if (hdr is not None and obj[0] == "phi" and len(obj) == 3
+                    and isinstance(obj[2], int) and obj[2] not in hdr[1]):
+                return False
             return obj[1] in body
-        return any(_defined_in(o, body) for o in obj)
+        return any(_defined_in(o, body, hdr) for o in obj)
     return False
 
 
@@ -679,14 +741,14 @@ def _at_header(an, st, j):
     """Entering loop header j: the values the loop defines are about to be defined again, so every path fact
     that names one of them (or an exec token made in the loop) is dropped, and the registers the loop writes
     take a version of the header's own.  Facts about values from before the loop stay true."""
-    body = an.loops[j]
+    body, hdr = an.loops[j], (j, an.loop_writes[j])
     s = st.copy()
     for r in an.loop_writes[j]:
         s.ver[r] = ("hdr", j, r)
-    s.facts = {a: v for a, v in s.facts.items() if not _defined_in(a, body)}
+    s.facts = {a: v for a, v in s.facts.items() if not _defined_in(a, body, hdr)}
     masks = {}
     for d, v in s.masks.items():
-        if not _defined_in(v, body):
+        if not _defined_in(v, body, hdr):
             masks[d] = v  # the value on this edge, made before the loop
         else:
             # keep only a bound from before the loop: the lanes of an exec
@@ -696,8 +758,8 @@ def _at_header(an, st, j):
                 masks[d] = ("sub", e)
     s.masks = masks
     s.scc = None
-    s.vuni = {r: v for r, v in s.vuni.items() if not _defined_in(v, body)}
-    s.vbool = {r: v for r, v in s.vbool.items() if not _defined_in(v, body)}
+    s.vuni = {r: v for r, v in s.vuni.items() if not _defined_in(v, body, hdr)}
+    s.vbool = {r: v for r, v in s.vbool.items() if not _defined_in(v, body, hdr)}
     if _defined_in(s.exec, body):
         s.exec = ("hdr", j, "exec", _outside(an, s.exec, body))
         s.nonempty = frozenset(x for x in s.nonempty if not _defined_in(x, body))

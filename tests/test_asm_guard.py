@@ -102,3 +102,44 @@ def test_only_functions_with_inline_assembly_are_checked_and_allowlist_applies()
     asm = k(LOAD + "\tv_mov_b32_e32 v1, v50\n\ts_waitcnt vmcnt(0)\n\ts_endpgm\n")
     assert hazards(asm) == ["k: v_mov_b32_e32 v1, v50"]
     assert hazards(asm, allowed=["k: v_mov_b32_e32 v1, v50"]) == []
+
+
+def test_a_load_under_two_conditions_and_an_exit_on_one_of_them():
+    # if (c && j == 0) load; if (!c) use (no wait): the load and the use
+    # never meet, since the load implies c
+    body = ("\tv_mov_b64_e32 v[4:5], s[6:7]\n\tv_cmp_lt_i64_e64 s[12:13], s[8:9], v[4:5]\n"
+            "\ts_cmp_eq_u32 s10, 0\n\ts_cselect_b64 s[14:15], -1, 0\n"
+            "{both}\ts_andn2_b64 vcc, exec, s[14:15]\n\ts_cbranch_vccnz .LBB0_2\n; %bb.1:\n" + LOAD +
+            ".LBB0_2:\n\ts_andn2_b64 vcc, exec, s[12:13]\n\ts_cbranch_vccnz .LBB0_4\n; %bb.3:\n"
+            "\ts_waitcnt vmcnt(0)\n\ts_branch .LBB0_5\n.LBB0_4:\n\tv_mov_b32_e32 v1, v50\n.LBB0_5:\n\ts_endpgm\n")
+    assert hazards(k(body.format(both="\ts_and_b64 s[14:15], s[12:13], s[14:15]\n"))) == []
+    # the load under j == 0 alone: with !c it is still in flight at the use
+    assert hazards(k(body.format(both=""))) == ["k: v_mov_b32_e32 v1, v50"]
+
+
+def test_a_uniform_copy_made_on_two_paths_keeps_its_value_through_joins_and_the_loop():
+    # v[4:5] holds s[6:7] on both paths into the loop (s6 differs between
+    # them); a flag keeps the paths apart until inside the loop, where they
+    # join.  The loop never writes s[6:7] or v[4:5], so the comparison against
+    # v[4:5] names one value in every iteration and the recomputed comparison
+    # prunes the use on the side without the wait.
+    asm = k("\ts_cbranch_scc1 .LBB0_1\n; %bb.0:\n\ts_add_u32 s6, s6, 1\n\tv_mov_b64_e32 v[4:5], s[6:7]\n"
+            "\ts_mov_b64 s[20:21], -1\n\ts_branch .LBB0_2\n"
+            ".LBB0_1:\n\tv_mov_b64_e32 v[4:5], s[6:7]\n\ts_mov_b64 s[20:21], 0\n"
+            ".LBB0_2:\n\ts_and_b64 vcc, exec, s[20:21]\n\ts_cbranch_vccz .LBB0_3\n; %bb.a:\n\ts_nop 0\n"
+            ".LBB0_3:\n\ts_mov_b64 s[20:21], 0\n\ts_branch .LBB0_4\n"
+            ".LBB0_4:\n\tv_cmp_lt_i64_e64 s[12:13], s[8:9], v[4:5]\n" + LOAD +
+            "\ts_and_b64 vcc, exec, s[12:13]\n\ts_cbranch_vccz .LBB0_6\n; %bb.5:\n\ts_waitcnt vmcnt(0)\n"
+            ".LBB0_6:\n\tv_cmp_ge_i64_e32 vcc, s[8:9], v[4:5]\n\ts_cbranch_vccnz .LBB0_8\n; %bb.7:\n"
+            "\tv_mov_b32_e32 v1, v50\n.LBB0_8:\n\ts_waitcnt vmcnt(0)\n\ts_add_i32 s2, s2, -1\n"
+            "\ts_cmp_lg_u32 s2, 0\n\ts_cbranch_scc1 .LBB0_2\n; %bb.9:\n\ts_endpgm\n")
+    assert hazards(asm) == []
+    # s6 written inside the loop: the check names v[4:5]'s value after the
+    # version of s[6:7] it was copied from, and a name the loop redefines does
+    # not survive its header, so the use is reported (a conservative answer)
+    assert hazards(asm.replace("\ts_add_i32 s2, s2, -1\n", "\ts_add_i32 s2, s2, -1\n\ts_add_u32 s6, s6, 1\n")) == \
+        ["k: v_mov_b32_e32 v1, v50"]
+    # v[4:5] refilled inside the loop from another register: a new value
+    # between the two comparisons is caught as before
+    assert hazards(asm.replace("\ts_cbranch_vccz .LBB0_6\n; %bb.5:", "\tv_mov_b64_e32 v[4:5], s[16:17]\n"
+                               "\ts_cbranch_vccz .LBB0_6\n; %bb.5:")) == ["k: v_mov_b32_e32 v1, v50"]
