@@ -67,9 +67,15 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const char* p) {
 // compiler's wait-count insertion does not see them; left to it, it drains
 // every outstanding load (including the next page's) before the first MFMA
 // of each page.  Their completion is awaited explicitly with wait_loads.
+//
+// Every K/V byte is read once per launch, so the 16-byte loads and the V
+// DMA carry the non-temporal (nt) cache policy: a plain 2 GiB streaming read
+// on MI355X moved 6.2-6.3 TB/s with ordinary 16-byte loads and 7.0-7.1 TB/s
+// with nt ones.  The FP8 form's 8-byte K loads stay ordinary: with nt they
+// made that decode about 20% slower.
 __device__ __forceinline__ u32x4 gload16(const void* p) {
     u32x4 r;
-    asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(r) : "v"(p) : "memory");
+    asm volatile("global_load_dwordx4 %0, %1, off nt" : "=v"(r) : "v"(p) : "memory");
     return r;
 }
 __device__ __forceinline__ u32x2 gload8(const void* p) {
@@ -85,10 +91,10 @@ __device__ __forceinline__ u32x2 fp8x4_to_bf16(uint32_t c) {
     return u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
 }
 // 16 bytes per lane, HBM -> LDS: lane l's bytes land at lds + 16 l (lds is
-// wave-uniform, passed in M0).
+// wave-uniform, passed in M0), non-temporal.
 __device__ __forceinline__ void dma16(const void* g, const char* lds) {
     const uint32_t m = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)lds;
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(m) : "memory", "m0");
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt" ::"v"(g), "s"(m) : "memory", "m0");
 }
 // Wait until at most N of this wave's vector-memory operations are in
 // flight (loads complete in issue order).  The memory clobber keeps LDS

@@ -7,7 +7,9 @@
 // null), and does nothing with the data but fold it into one register, so
 // the time is that of the reads alone.  One workgroup of slice_bytes / 16
 // lanes reads a whole slice with 16-byte loads, eight slices per round
-// (eight loads in flight per lane); workgroups stride over the slices.
+// (eight loads in flight per lane); workgroups stride over the slices.  The
+// loads are ordinary or non-temporal (nt), the policy the decode's K and V
+// loads use.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -15,20 +17,25 @@ namespace {
 
 constexpr int kUnroll = 8;
 
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+template <bool kNT>
 __global__ __launch_bounds__(256) void probe_read_slices_kernel(const char* __restrict__ base,
                                                                  const long long* __restrict__ offs, long long n,
                                                                  int slice_bytes, unsigned* __restrict__ sink) {
     const long long lane_off = (long long)threadIdx.x * 16;
     unsigned acc = 0;
     for (long long i0 = (long long)blockIdx.x * kUnroll; i0 < n; i0 += (long long)gridDim.x * kUnroll) {
-        uint4 v[kUnroll];
+        u32x4 v[kUnroll];
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
             const long long i = i0 + u;
-            v[u] = make_uint4(0, 0, 0, 0);
+            v[u] = u32x4{0, 0, 0, 0};
             if (i < n) {
                 const long long o = offs ? offs[i] : i * (long long)slice_bytes;
-                v[u] = *reinterpret_cast<const uint4*>(base + o + lane_off);
+                const u32x4* p = reinterpret_cast<const u32x4*>(base + o + lane_off);
+                if constexpr (kNT) v[u] = __builtin_nontemporal_load(p);
+                else v[u] = *p;
             }
         }
 #pragma unroll
@@ -46,13 +53,19 @@ extern "C" {
 // at most 4096; base + offs[i] must be 16-byte aligned and the slice inside
 // the buffer (the caller's contract; nothing is checked on the device).
 // sink: 256 unsigned words of device memory.  blocks: workgroups to launch.
+// nt: 0 ordinary loads, 1 non-temporal loads.
 int probe_read_slices(const void* base, const long long* offs, long long n, int slice_bytes, unsigned* sink,
-                      int blocks, hipStream_t stream) {
-    if (!base || !sink || n < 0 || slice_bytes < 16 || slice_bytes > 4096 || slice_bytes % 16 || blocks < 1)
+                      int blocks, int nt, hipStream_t stream) {
+    if (!base || !sink || n < 0 || slice_bytes < 16 || slice_bytes > 4096 || slice_bytes % 16 || blocks < 1 ||
+        (nt != 0 && nt != 1))
         return (int)hipErrorInvalidValue;
     if (n == 0) return 0;
-    hipLaunchKernelGGL(probe_read_slices_kernel, dim3((unsigned)blocks), dim3((unsigned)(slice_bytes / 16)), 0,
-                       stream, static_cast<const char*>(base), offs, n, slice_bytes, sink);
+    const dim3 grid((unsigned)blocks), block((unsigned)(slice_bytes / 16));
+    const char* b = static_cast<const char*>(base);
+    if (nt)
+        hipLaunchKernelGGL(probe_read_slices_kernel<true>, grid, block, 0, stream, b, offs, n, slice_bytes, sink);
+    else
+        hipLaunchKernelGGL(probe_read_slices_kernel<false>, grid, block, 0, stream, b, offs, n, slice_bytes, sink);
     return (int)hipGetLastError();
 }
 

@@ -183,22 +183,22 @@ def read_ceiling(args):
     """The practical HBM read ceiling: a kernel that only reads (libattn_probe.so), timed with HIP events
     over K launches, on (1) a 2 GiB buffer in 4 KiB slices, (2) the 4 KiB K and V slices of workload 5's
     decode pool and (3) the 2 KiB K and V slices of workload 9's FP8 pool, (sequence, kv head, page) in the
-    streaming decode's order, from pools far larger than the MALL.  Context for the decode's rate, not a
-    replacement for the 8 TB/s peak."""
+    streaming decode's order, from pools far larger than the MALL; each with ordinary and with non-temporal
+    16-byte loads.  Context for the decode's rate, not a replacement for the 8 TB/s peak."""
     import ctypes
     lib = ctypes.CDLL(os.path.join(ROOT, "attention_causal_gqa_amd", "libattn_probe.so"))
     vp = ctypes.c_void_p
-    lib.probe_read_slices.argtypes = [vp, vp, ctypes.c_longlong, ctypes.c_int, vp, ctypes.c_int, vp]
+    lib.probe_read_slices.argtypes = [vp, vp, ctypes.c_longlong, ctypes.c_int, vp, ctypes.c_int, ctypes.c_int, vp]
     lib.probe_read_slices.restype = ctypes.c_int
     dev = torch.device("cuda:0")
     blocks = torch.cuda.get_device_properties(dev).multi_processor_count * 8
     sink = torch.zeros(256, dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream()
 
-    def timed(base, offs, n, slice_bytes):
+    def timed(base, offs, n, slice_bytes, nt):
         def go():
             rc = lib.probe_read_slices(base.data_ptr(), None if offs is None else offs.data_ptr(), n, slice_bytes,
-                                       sink.data_ptr(), blocks, ctypes.c_void_p(stream.cuda_stream))
+                                       sink.data_ptr(), blocks, nt, ctypes.c_void_p(stream.cuda_stream))
             if rc != 0:
                 raise RuntimeError(f"probe_read_slices failed: {rc}")
         for _ in range(args.warmup):
@@ -211,8 +211,13 @@ def read_ceiling(args):
         e1.record(stream)
         torch.cuda.synchronize()
         ms = e0.elapsed_time(e1) / args.steps
-        return {"slices": int(n), "slice_bytes": slice_bytes, "bytes": int(n) * slice_bytes, "ms": round(ms, 4),
+        return {"slices": int(n), "slice_bytes": slice_bytes, "bytes": int(n) * slice_bytes,
+                "loads": "non-temporal" if nt else "ordinary", "ms": round(ms, 4),
                 "gbps": round(n * slice_bytes / (ms / 1e3) / 1e9, 1)}
+
+    def both(name, base, offs, n, slice_bytes):
+        out[name] = timed(base, offs, n, slice_bytes, 0)
+        out[name + "_nt"] = timed(base, offs, n, slice_bytes, 1)
 
     def decode_slices(seq_lens, block_table, P, Hkv, page_size, slice_bytes):
         """Byte offsets of the K and V slices one decode reads, in its order, in a K pool then V pool."""
@@ -227,7 +232,7 @@ def read_ceiling(args):
 
     out = {}
     big = torch.ones(2 << 30, dtype=torch.uint8, device=dev)
-    out["contiguous"] = timed(big, None, big.numel() // 4096, 4096)
+    both("contiguous", big, None, big.numel() // 4096, 4096)
     del big
     shp = synth.WORKLOADS[5]["decode"]
     inp = synth.paged_inputs(shp, seed=105)
@@ -235,7 +240,7 @@ def read_ceiling(args):
     sb = shp.page_size * shp.d * 2
     pool = torch.ones(2 * P * shp.Hkv * sb, dtype=torch.uint8, device=dev)  # K pool, then V pool
     offs = decode_slices(inp.seq_lens, inp.block_table, P, shp.Hkv, shp.page_size, sb)
-    out["decode_pages_w5"] = timed(pool, offs, offs.numel(), sb)
+    both("decode_pages_w5", pool, offs, offs.numel(), sb)
     del pool, inp
     shp = synth.WORKLOADS[9]["decode_fp8"]
     inp = synth.fp8_paged_inputs(shp, seed=109)
@@ -243,7 +248,7 @@ def read_ceiling(args):
     sb = shp.page_size * shp.d
     pool = torch.ones(2 * P * shp.Hkv * sb, dtype=torch.uint8, device=dev)
     offs = decode_slices(inp.seq_lens, inp.block_table, P, shp.Hkv, shp.page_size, sb)
-    out["decode_pages_w9_fp8"] = timed(pool, offs, offs.numel(), sb)
+    both("decode_pages_w9_fp8", pool, offs, offs.numel(), sb)
     out.update({"blocks": blocks, "steps": args.steps})
     print(json.dumps({"read_ceiling": out}), flush=True)
 

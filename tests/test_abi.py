@@ -384,11 +384,12 @@ def test_read_probe_library_loads_and_rejects_bad_arguments():
     probe = ctypes.CDLL(os.path.join(os.path.dirname(A.__file__), "libattn_probe.so"))
     f = probe.probe_read_slices
     vp = ctypes.c_void_p
-    f.argtypes = [vp, vp, ctypes.c_longlong, ctypes.c_int, vp, ctypes.c_int, vp]
+    f.argtypes = [vp, vp, ctypes.c_longlong, ctypes.c_int, vp, ctypes.c_int, ctypes.c_int, vp]
     f.restype = ctypes.c_int
-    good = dict(base=FAKE, offs=None, n=4, slice_bytes=4096, sink=FAKE, blocks=8)
+    good = dict(base=FAKE, offs=None, n=4, slice_bytes=4096, sink=FAKE, blocks=8, nt=1)
     for bad in (dict(base=None), dict(sink=None), dict(n=-1), dict(slice_bytes=8), dict(slice_bytes=4100),
-                dict(slice_bytes=8192), dict(blocks=0)):
+                dict(slice_bytes=8192), dict(blocks=0), dict(nt=2), dict(nt=-1)):
         a = {**good, **bad}
-        assert f(a["base"], a["offs"], a["n"], a["slice_bytes"], a["sink"], a["blocks"], None) != 0, bad
-    assert f(FAKE, None, 0, 4096, FAKE, 8, None) == 0  # nothing to read: no launch
+        assert f(a["base"], a["offs"], a["n"], a["slice_bytes"], a["sink"], a["blocks"], a["nt"], None) != 0, bad
+    assert f(FAKE, None, 0, 4096, FAKE, 8, 0, None) == 0  # nothing to read: no launch
+    assert f(FAKE, None, 0, 4096, FAKE, 8, 1, None) == 0
