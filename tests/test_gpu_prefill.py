@@ -145,6 +145,32 @@ def test_lse_is_optional_and_out_is_identical():
     assert l2 is None and torch.equal(o1.cpu(), o2.cpu())
 
 
+# ------------------------------------------------------------------ many (sequence, kv head) pairs
+# Batches with 100 and 256 (sequence, kv head) pairs, so the workgroup order
+# cycles over many pairs (partial last blocks, d 64 and 128); each result is
+# also compared bit for bit with the same sequence run alone, which launches
+# a different set of workgroups.
+PAIR_SHAPES = [
+    # B, Hq, Hkv, T, d
+    (16, 32, 16, 300, 128),  # 256 pairs, three blocks of 128 tokens per pair, the last of 44
+    (2, 128, 16, 300, 128),  # 32 pairs, g = 8: 10 blocks of 32 tokens per pair
+    (16, 16, 16, 520, 64),   # 256 pairs, d 64: blocks of 256, 256 and 8 tokens
+    (25, 8, 4, 300, 64),     # 100 pairs
+]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,T,d", PAIR_SHAPES)
+def test_bf16_many_pairs(B, Hq, Hkv, T, d):
+    shp = synth.PrefillShape(B, Hq, Hkv, T, d, torch.bfloat16)
+    q, k, v = synth.prefill_inputs(shp, seed=3000 + B + T)
+    out, lse = check_full(q, k, v, synth.fp32_scale(d), TOL_BF16, f"bf16 many pairs B{B} Hq{Hq} Hkv{Hkv} T{T} d{d}")
+    # The same sequence alone: its rows must come out bit for bit the same.
+    for b in (0, B - 1):
+        o1, l1 = run_prefill(q[b : b + 1], k[b : b + 1], v[b : b + 1], synth.fp32_scale(d))
+        assert torch.equal(o1.cpu(), out[b : b + 1].cpu()), f"sequence {b} alone differs"
+        assert torch.equal(l1.cpu(), lse[b : b + 1].cpu()), f"sequence {b} alone differs (lse)"
+
+
 # ------------------------------------------------------------------ full-size workloads, whole output
 @pytest.mark.parametrize("workload", [3, 5])
 def test_full_size_prefill_whole_output(workload):
