@@ -83,10 +83,11 @@ def environment():
 
 
 def sample_gfx_clock(launch, seconds=1.5, skip=0.8):
-    """GFX clock (MHz) that amdsmi reports while `launch` runs back to back for `seconds`, or None when amdsmi is
-    not usable on this host.  The firmware's metrics table lags the GPU by about half a second (the reading stayed
-    at its idle value for ~0.5 s after a kernel loop started), so samples from the first `skip` seconds are
-    dropped.  Per-XCD current clocks when the table has them, else the single current clock."""
+    """GFX clock (MHz) and socket power (W) that amdsmi reports while `launch` runs back to back for `seconds`,
+    or None when amdsmi is not usable on this host.  The firmware's metrics table lags the GPU by about half a
+    second (the reading stayed at its idle value for ~0.5 s after a kernel loop started), so samples from the
+    first `skip` seconds are dropped.  Per-XCD current clocks when the table has them, else the single current
+    clock; the power cap beside the power, so a kernel held at the cap shows as such."""
     try:
         import threading
 
@@ -94,8 +95,15 @@ def sample_gfx_clock(launch, seconds=1.5, skip=0.8):
 
         amdsmi.amdsmi_init()
         handle = amdsmi.amdsmi_get_processor_handles()[0]
-        samples, done = [], threading.Event()
+        samples, watts, done = [], [], threading.Event()
         t_start = time.perf_counter()
+
+        def power():
+            try:
+                w = amdsmi.amdsmi_get_power_info(handle).get("current_socket_power")
+                return float(w) if isinstance(w, (int, float)) and w > 0 else None
+            except Exception:
+                return None
 
         def read():
             try:
@@ -115,6 +123,9 @@ def sample_gfx_clock(launch, seconds=1.5, skip=0.8):
                     v = read()
                     if v is not None and t >= skip:
                         samples.append(v)
+                    w = power() if t >= skip else None
+                    if w is not None:
+                        watts.append(w)
                 except Exception:
                     pass
                 time.sleep(0.01)
@@ -128,14 +139,21 @@ def sample_gfx_clock(launch, seconds=1.5, skip=0.8):
             torch.cuda.synchronize()
         done.set()
         th.join()
+        cap = None
+        try:
+            c = amdsmi.amdsmi_get_power_cap_info(handle).get("power_cap")
+            cap = round(float(c) / 1e6, 1) if isinstance(c, (int, float)) and c > 0 else None  # reported in uW
+        except Exception:
+            pass
         amdsmi.amdsmi_shut_down()
         if not samples:
             return None
         means = [float(np.mean(v)) for v in samples]
         return {"mhz_median": round(float(np.median(means)), 1), "mhz_min": round(float(min(means)), 1),
                 "per_xcd_last": samples[-1], "samples": len(samples),
-                "note": f"amdsmi current GFX clock (mean over XCDs) while the dominant kernel ran back to back; "
-                        f"samples after the first {skip} s of {seconds} s"}
+                "socket_w_median": round(float(np.median(watts)), 1) if watts else None, "power_cap_w": cap,
+                "note": f"amdsmi current GFX clock (mean over XCDs) and socket power while the dominant kernel ran "
+                        f"back to back; samples after the first {skip} s of {seconds} s"}
     except Exception:
         return None
 
