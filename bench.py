@@ -12,18 +12,23 @@ synthetic tensors, resident in HBM before timing.
 Prints one JSON line.  ``value`` is the step's roofline fraction: the time the
 step's algorithmic work takes at MI355X peak (prefill flops at the bf16 MFMA
 peak plus decode bytes at the HBM peak) divided by the measured step time.
-After the warm-up, untimed steps run until 30 have run in all (the GPU clock
-settles over the first few tens of steps).  The timed region is exactly K
+After the warm-up, untimed steps run until 30 have run in all and the GPU
+has been busy for 0.5 s (its speed settles over the first tens of ms).  The timed region is exactly K
 steps between two synchronizations: ``ms_per_step`` is their host-clock
-time, and ``kernel_ms_per_step`` with the median and p90 in ``step_events``
-comes from timing markers on the launch stream at each of those steps' ends.
+time, and ``kernel_ms_per_step`` the time between two timing markers on the
+launch stream before the first and after the last of those steps (with
+``--flush``, a marker pair around each step, after its flush).  The
+per-step median, p90 and minimum in ``step_events`` come from a later pass
+of K steps with one marker at each step's end.
 Per-part times come from a later pass of K steps with events around each
-part, queued behind a short GPU sleep so that the events time the kernels;
-in the two-stream step those events slow the step, so per-part times there
-are upper bounds.  A workload with a single part also times K queued
-launches between one pair of events, and in a two-part step the dominant
-kernel is timed alone that way: ``roofline.achieved`` is its average launch
-duration.  ``environment`` names the GPU, ROCm and torch, and the GFX clock
+part; in the two-stream step those events slow the step, so per-part times
+there are upper bounds.  A workload with a single part also times K
+back-to-back launches between one pair of events, and in a two-part step
+the dominant kernel is timed alone that way: ``roofline.achieved`` is its
+average launch duration.  These passes run in the steady state the timed
+region leaves (no GPU sleep before them, which would let the idle GPU boost
+its clock), except where the host issues a step more slowly than the GPU
+runs it.  ``environment`` names the GPU, ROCm and torch, and the GFX clock
 amdsmi reports while the dominant kernel runs.
 
     python bench.py [--steps K] [--warmup W] [--workload 5|3|4|6|7|8|9|10] [--no-cpu-baseline] [--flush]
@@ -65,7 +70,8 @@ PEAK_BF16_FLOPS = 2.5e15  # MI355X dense bf16 MFMA, published
 PEAK_HBM_BYTES = 8.0e12   # MI355X HBM3E, published
 METRIC = "prefill TFLOP/s and paged-decode HBM GB/s, as fraction of MI355X peak"
 PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
-SETTLE_STEPS = 30  # untimed steps (warm-up included) before the timed region
+SETTLE_STEPS = 30  # untimed steps (warm-up included) before the timed region, at least
+SETTLE_SECONDS = 0.5  # and at least this much GPU-busy time
 
 
 def environment():
@@ -578,45 +584,74 @@ def main():
 
     for _ in range(args.warmup):
         step()
-    # Settling: the GPU's clock takes some tens of steps to settle after the
-    # process starts (the step's event span fell from 0.83-0.89 ms to 0.78 ms
-    # over the first ~25 steps of workload 5), so untimed steps are added
-    # until SETTLE_STEPS have run in all.
+    # Settling: the GPU's speed takes some time to settle once it is busy (the
+    # step's event span fell from 0.83-0.89 ms to 0.78 ms over the first ~25
+    # steps of workload 5; back-to-back workload-3 prefills took 95 us each
+    # at first and ~80 us after some 100 launches), so untimed steps are
+    # added until SETTLE_STEPS have run in all and the GPU has been busy for
+    # SETTLE_SECONDS (steps issued in batches, each batch synchronized).
     settle = max(0, SETTLE_STEPS - args.warmup)
     for _ in range(settle):
         step()
     torch.cuda.synchronize()
+    t_settle = time.perf_counter()
+    while time.perf_counter() - t_settle < SETTLE_SECONDS:
+        for _ in range(8):
+            step()
+        settle += 8
+        torch.cuda.synchronize()
 
     # Timed region: exactly K steps between two synchronizations on the host
-    # clock.  The only events in it are one timing marker on the launch
-    # stream before the first step and one at the end of each step (with
-    # --flush, one more after each step's flush), so the per-step event times
-    # come from the same steps.  Events around the parts on their own streams
-    # are left out of it: they slowed the two-stream step of workload 5 by
-    # about 7% (0.720 against 0.671 ms on one box), the step-end markers by
-    # about 1%.
+    # clock, with one timing marker on the launch stream before the first
+    # step and one after the last (with --flush, a marker after each step's
+    # flush and one at each step's end, so that the flush stays out).  Events
+    # around the parts on their own streams slowed the two-stream step of
+    # workload 5 by about 7%, so they stay out of it.
     marks = [timing_event() for _ in range(args.steps + 1)]
     starts = [timing_event() if flush_buf is not None else None for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     marks[0].record(stream)
     for s in range(args.steps):
-        step(mark=(starts[s], marks[s + 1]))
+        step(mark=(starts[s], marks[s + 1]) if flush_buf is not None else None)
+    if flush_buf is None:
+        marks[args.steps].record(stream)
     issued = time.perf_counter() - t0
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    step_events = np.asarray([(starts[s] if flush_buf is not None else marks[s]).elapsed_time(marks[s + 1])
-                              for s in range(args.steps)])
-    step_ms = float(step_events.mean())
+    if flush_buf is not None:
+        step_events = np.asarray([starts[s].elapsed_time(marks[s + 1]) for s in range(args.steps)])
+        step_ms = float(step_events.mean())
+    else:
+        step_ms = marks[0].elapsed_time(marks[args.steps]) / args.steps
+        # The per-step distribution: K more steps with a marker at each end.
+        marks2 = [timing_event() for _ in range(args.steps + 1)]
+        torch.cuda.synchronize()
+        marks2[0].record(stream)
+        for s in range(args.steps):
+            step(mark=(None, marks2[s + 1]))
+        torch.cuda.synchronize()
+        step_events = np.asarray([marks2[s].elapsed_time(marks2[s + 1]) for s in range(args.steps)])
+
+    # The passes below time kernels back to back in the steady state the
+    # timed region left behind.  A GPU sleep before a pass would let the
+    # host queue every launch first, but the idle GPU then gains power
+    # headroom and runs the following kernels at a boosted clock (workload 3:
+    # 78 us per launch behind a sleep against 80-95 us back to back), so the
+    # sleep is used only where the host issues a step more slowly than the GPU
+    # runs it (then back-to-back launches would time the host).
+    host_bound = issued / args.steps > 0.5 * step_ms / 1e3
+
+    def lead_in():
+        if host_bound:
+            torch.cuda._sleep(200_000 * args.steps)
 
     # Per-part times (diagnostic, after the timed region): K more steps with
-    # events around every part, queued behind a short GPU sleep so that the
-    # events time the kernels and not the host's launch latency.  In a
-    # two-stream step these events slow the step (see above): the per-part
-    # times inside it are upper bounds.
+    # events around every part.  In a two-stream step these events slow the
+    # step (see above): the per-part times inside it are upper bounds.
     evs = [new_events() for _ in range(args.steps)]
     torch.cuda.synchronize()
-    torch.cuda._sleep(200_000 * args.steps)
+    lead_in()
     for s in range(args.steps):
         step(evs[s])
     torch.cuda.synchronize()
@@ -627,7 +662,7 @@ def main():
     if concurrent:  # each part alone (one after the other), for reference
         evs2 = [new_events() for _ in range(args.steps)]
         torch.cuda.synchronize()
-        torch.cuda._sleep(200_000 * args.steps)
+        lead_in()
         for s in range(args.steps):
             step(evs2[s], seq=True)
         torch.cuda.synchronize()
@@ -635,14 +670,15 @@ def main():
                     for n in names}
     dom_block_ms = None
     if len(names) > 1 and flush_buf is None:
-        # The dominant kernel alone, K queued launches between one pair of
+        # The dominant kernel alone, K back-to-back launches between one pair of
         # events on the launch stream: its average launch duration, which the
         # roofline uses (a per-step event pair would also hold the gap after
         # the other part's last kernel).
         dom = max(names, key=lambda n: ms[n])
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
-        torch.cuda._sleep(200_000 * args.steps)
+        for _ in range(3):  # back to the steady state after the synchronization
+            work[dom]()
         e0.record(stream)
         for _ in range(args.steps):
             work[dom]()
@@ -650,13 +686,16 @@ def main():
         torch.cuda.synchronize()
         dom_block_ms = e0.elapsed_time(e1) / args.steps
     if len(names) == 1 and flush_buf is None:
-        # One part per step: also time K queued launches between one pair of
+        # One part per step: also time K back-to-back launches between one pair of
         # events, so that a short kernel's time does not carry the cost of an
         # event pair per launch (a few microseconds).  (With --flush the
         # per-step event pairs are kept: they leave out each step's flush.)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
-        torch.cuda._sleep(200_000 * args.steps)
+        lead_in()
+        if not host_bound:
+            for _ in range(3):  # back to the steady state after the synchronization
+                step()
         e0.record(stream)
         for _ in range(args.steps):
             step()
@@ -774,14 +813,14 @@ def main():
                 "source_hash": src}
     if dom_block_ms is not None:
         # In a two-part step the kernel's own rate is its average launch
-        # duration alone (K queued launches, measured in this run); with two
+        # duration alone (K back-to-back launches, measured in this run); with two
         # streams its duration inside the step is longer, as the parts share
         # the chip (achieved_in_step).
         r = ms[dom] / dom_block_ms
         roof["achieved_in_step"] = roof["achieved"]
         roof["achieved"] = round(roof["achieved"] * r, 1)
         roof["frac"] = round(roof["frac"] * r, 4)
-        roof["timed"] = f"alone: {args.steps} queued launches between one pair of HIP events"
+        roof["timed"] = f"alone: {args.steps} back-to-back launches between one pair of HIP events"
 
     cfg = {"workload": synth.WORKLOAD_NAMES[args.workload]}
     if pre_shape is not None:
@@ -811,8 +850,9 @@ def main():
         "step_events": {"ms_median": round(float(np.median(step_events)), 4),
                         "ms_p90": round(float(np.percentile(step_events, 90)), 4),
                         "ms_min": round(float(step_events.min()), 4),
-                        "note": "timing markers on the launch stream at each of the K timed steps' ends (the steps "
-                                "of ms_per_step)"},
+                        "note": ("marker pairs around each of the K timed steps, after the step's flush"
+                                 if flush_buf is not None else
+                                 "a later pass of K steps with a timing marker at each step's end")},
         "settle_steps": settle,
         "host_issue_ms_per_step": round(issued * 1e3 / args.steps, 4),
         **({"schedule": "decode and prefill on two HIP streams, joined once per step",
