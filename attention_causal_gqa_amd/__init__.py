@@ -1,5 +1,6 @@
 """Causal MHA/GQA attention for MI355X (gfx950): bf16 MFMA prefill (dense, ragged over packed tokens, or
-chunked over a paged cache), paged split-KV decode (bf16 or FP8 E4M3 cache), and the paged-cache KV append.
+chunked over a paged cache, alone or fused with the chunk's KV append), paged split-KV decode (bf16 or FP8 E4M3
+cache), and the paged-cache KV append.
 
 The compute lives in ``libattn.so`` (hand-written HIP kernels behind the C ABI
 declared in ``include/attn.h``); this package is its ctypes binding, with the
@@ -26,6 +27,7 @@ from ._binding import (  # noqa: F401
     attn_last_error_message,
     attn_prefill,
     attn_prefill_paged,
+    attn_prefill_paged_append,
     attn_prefill_varlen,
     attn_status_string,
     attn_validate_chunk_metadata,

@@ -59,6 +59,9 @@ def load_library():
     lib.attn_prefill_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, f32, i32,
                                        vp]
     lib.attn_prefill_paged.restype = i32
+    lib.attn_prefill_paged_append.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
+                                              i32, f32, i32, vp]
+    lib.attn_prefill_paged_append.restype = i32
     lib.attn_prefill_varlen.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32, vp]
     lib.attn_prefill_varlen.restype = i32
     lib.attn_validate_varlen_metadata.argtypes = [vp, i32, i32, i32]
@@ -201,6 +204,46 @@ def attn_prefill_paged(q, k_pages, v_pages, block_table, seq_lens, out=None, lse
                                              _ptr(seq_lens), _ptr(out), None if lse is False else _ptr(lse), B, Hq,
                                              Hkv, Tq, d, page_size, P, W, float(scale), _dtype_code(q),
                                              _stream(stream)))
+    return out, (None if lse is False else lse)
+
+
+def attn_prefill_paged_append(q, k_new, v_new, k_pages, v_pages, block_table, seq_lens, out=None, lse=None,
+                              scale=None, stream=None):
+    """KV append + chunked prefill in one launch.  q [B,Hq,Tq,d]; k_new/v_new [B,Hkv,Tq,d] (the chunk's keys and
+    values, written into the pools in place); pools [P,Hkv,page,d]; block_table [B,W] int32; seq_lens [B] int32 =
+    lengths after the append (>= Tq) -> (out, lse fp32 [B,Hq,Tq])."""
+    torch = _torch()
+    _require(q.dim() == 4 and k_new.dim() == 4 and k_new.shape == v_new.shape, "bad q / k_new / v_new shapes")
+    _require(k_pages.dim() == 4 and k_pages.shape == v_pages.shape, "bad page pool shapes")
+    B, Hq, Tq, d = q.shape
+    P, Hkv, page_size, dk = k_pages.shape
+    _require(dk == d, "page pools and q disagree on d")
+    _require(k_new.shape == (B, Hkv, Tq, d), "k_new and v_new must be [B, Hkv, Tq, d]")
+    _require(block_table.dim() == 2 and block_table.shape[0] == B and block_table.dtype == torch.int32,
+             "block_table must be int32 [B, W]")
+    _require(seq_lens.shape == (B,) and seq_lens.dtype == torch.int32, "seq_lens must be int32 [B]")
+    for n, t in (("q", q), ("k_new", k_new), ("v_new", v_new), ("k_pages", k_pages), ("v_pages", v_pages),
+                 ("block_table", block_table), ("seq_lens", seq_lens)):
+        _dense_on_gpu(n, t)
+    _require(q.dtype == k_new.dtype == v_new.dtype == k_pages.dtype == v_pages.dtype,
+             "q, k_new, v_new and the page pools must share a dtype")
+    W = block_table.shape[1]
+    with _alloc_stream(stream):
+        if out is None:
+            out = torch.empty_like(q)
+        if lse is None:
+            lse = torch.empty((B, Hq, Tq), dtype=torch.float32, device=q.device)
+    _dense_on_gpu("out", out)
+    _require(out.shape == q.shape and out.dtype == q.dtype, "out must match q")
+    if lse is not False:
+        _dense_on_gpu("lse", lse)
+        _require(lse.shape == (B, Hq, Tq) and lse.dtype == torch.float32, "lse must be float32 [B, Hq, Tq]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    _check(load_library().attn_prefill_paged_append(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_pages),
+                                                    _ptr(v_pages), _ptr(block_table), _ptr(seq_lens), _ptr(out),
+                                                    None if lse is False else _ptr(lse), B, Hq, Hkv, Tq, d,
+                                                    page_size, P, W, float(scale), _dtype_code(q), _stream(stream)))
     return out, (None if lse is False else lse)
 
 

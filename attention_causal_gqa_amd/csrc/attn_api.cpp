@@ -241,6 +241,54 @@ int attn_prefill_paged(const void* q, const void* k_pages, const void* v_pages, 
                     "attn_prefill_paged launch");
 }
 
+int attn_prefill_paged_append(const void* q, const void* k_new, const void* v_new, void* k_pages, void* v_pages,
+                              const int32_t* block_table, const int32_t* seq_lens, void* out, float* lse, int B, int Hq,
+                              int Hkv, int Tq, int d, int page_size, int num_pages, int max_pages_per_seq, float scale,
+                              int dtype, hipStream_t stream) {
+    g_last_error.clear();
+    if (dtype != ATTN_F32 && dtype != ATTN_BF16) return fail(ATTN_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+    if (B < 0 || Tq < 0) return fail(ATTN_ERR_INVALID_ARG, "B=%d, Tq=%d must be >= 0", B, Tq);
+    if (Hq < 1 || Hkv < 1) return fail(ATTN_ERR_INVALID_ARG, "Hq=%d, Hkv=%d must be >= 1", Hq, Hkv);
+    if (Hq % Hkv != 0) return fail(ATTN_ERR_INVALID_ARG, "Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
+    if (d < 1) return fail(ATTN_ERR_INVALID_ARG, "d=%d must be >= 1", d);
+    if (page_size < 1) return fail(ATTN_ERR_INVALID_ARG, "page_size=%d must be >= 1", page_size);
+    if (max_pages_per_seq < 1) return fail(ATTN_ERR_INVALID_ARG, "max_pages_per_seq=%d must be >= 1", max_pages_per_seq);
+    if (num_pages < 0) return fail(ATTN_ERR_INVALID_ARG, "num_pages=%d must be >= 0", num_pages);
+    if ((int64_t)max_pages_per_seq * page_size > 0x7fffffff)
+        return fail(ATTN_ERR_INVALID_ARG, "max_pages_per_seq * page_size overflows int");
+    if ((int64_t)Tq > (int64_t)max_pages_per_seq * page_size)
+        return fail(ATTN_ERR_INVALID_ARG, "Tq=%d exceeds the cache capacity max_pages_per_seq * page_size", Tq);
+    if ((int64_t)B * Hkv * Tq > 0x7fffffff) return fail(ATTN_ERR_INVALID_ARG, "B * Hkv * Tq overflows int");
+    if (!std::isfinite(scale)) return fail(ATTN_ERR_INVALID_ARG, "scale must be finite");
+    if (dtype != ATTN_BF16) return fail(ATTN_ERR_UNSUPPORTED, "fused append + chunked prefill supports ATTN_BF16 only");
+    if (d != 64 && d != 128)
+        return fail(ATTN_ERR_UNSUPPORTED, "fused append + chunked prefill supports d = 64 or 128, not %d", d);
+    if (page_size != kPageSize)
+        return fail(ATTN_ERR_UNSUPPORTED, "fused append + chunked prefill supports page_size = 16, not %d", page_size);
+    if (Hq / Hkv > kMaxPrefillGroup)
+        return fail(ATTN_ERR_UNSUPPORTED, "fused append + chunked prefill supports Hq/Hkv <= %d", kMaxPrefillGroup);
+    if (max_pages_per_seq > kMaxChunkTablePages)
+        return fail(ATTN_ERR_UNSUPPORTED, "fused append + chunked prefill supports max_pages_per_seq <= %d",
+                    kMaxChunkTablePages);
+    if (B == 0 || Tq == 0) return ATTN_OK;
+    if (!q || !k_new || !v_new || !k_pages || !v_pages || !block_table || !seq_lens || !out)
+        return fail(ATTN_ERR_INVALID_ARG,
+                    "q, k_new, v_new, k_pages, v_pages, block_table, seq_lens and out must be non-null");
+    if (!aligned(q, 16) || !aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(k_pages, 16) ||
+        !aligned(v_pages, 16) || !aligned(out, 16))
+        return fail(ATTN_ERR_INVALID_ARG, "q, k_new, v_new, k_pages, v_pages and out must be 16-byte aligned");
+    if (!aligned(block_table, 4) || !aligned(seq_lens, 4) || (lse && !aligned(lse, 4)))
+        return fail(ATTN_ERR_INVALID_ARG, "block_table, seq_lens and lse must be 4-byte aligned");
+    const int64_t rows_per_block = 256 / (Hq / Hkv);
+    const int64_t blocks = (Tq + rows_per_block - 1) / rows_per_block * B * Hkv;
+    if (blocks > kMaxGrid) return fail(ATTN_ERR_INVALID_ARG, "problem too large: %lld workgroups", (long long)blocks);
+
+    attn::PrefillArgs a{q, k_pages, v_pages, out, lse, B, Hq, Hkv, Tq, d, scale};
+    return from_hip(attn::launch_prefill_paged_append_bf16(a, k_new, v_new, k_pages, v_pages, block_table, seq_lens,
+                                                           max_pages_per_seq, stream),
+                    "attn_prefill_paged_append launch");
+}
+
 int attn_prefill_varlen(const void* q, const void* k, const void* v, void* out, float* lse, const int32_t* cu_seqlens,
                         int num_seqs, int total_tokens, int max_seqlen, int Hq, int Hkv, int d, float scale,
                         int dtype, hipStream_t stream) {

@@ -53,6 +53,12 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream);
 // [num_pages, Hkv, 16, d], a.T is the chunk length; block_table [B, W].
 hipError_t launch_prefill_paged_bf16(const PrefillArgs& a, const int32_t* block_table, const int32_t* seq_lens, int W,
                                      hipStream_t stream);
+// The chunked prefill with the chunk's own keys and values in k_new / v_new
+// [B, Hkv, T, d] (not yet in the pools a.k / a.v); the launch also writes
+// them into the pools through k_pages / v_pages (the same pools, writable).
+hipError_t launch_prefill_paged_append_bf16(const PrefillArgs& a, const void* k_new, const void* v_new, void* k_pages,
+                                            void* v_pages, const int32_t* block_table, const int32_t* seq_lens, int W,
+                                            hipStream_t stream);
 // Ragged batch packed along the token axis: a.q / a.out [N, Hq, d], a.k / a.v
 // [N, Hkv, d], a.lse [N, Hq]; a.B sequences, cu_seqlens [B+1]; a.T is the
 // longest sequence.

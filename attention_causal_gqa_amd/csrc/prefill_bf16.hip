@@ -56,8 +56,9 @@ constexpr int kPage = 16;   // tokens per page of a paged cache
 constexpr int kMaxTablePages = 8192;  // block-table entries staged in LDS (contexts up to 131072 tokens)
 
 // Forms of the prefill kernel: dense [B, H, T, d] tensors; chunked prefill
-// over a paged cache; a ragged batch packed along the token axis.
-enum PrefillMode { kDense = 0, kPagedMode = 1, kVarlenMode = 2 };
+// over a paged cache; a ragged batch packed along the token axis; chunked
+// prefill that also appends the chunk's keys and values to the paged cache.
+enum PrefillMode { kDense = 0, kPagedMode = 1, kVarlenMode = 2, kAppendMode = 3 };
 
 // XOR swizzle of 16-byte chunks within an LDS row of CPR chunks: chunk c of
 // row r is stored at position c ^ swz(r).  With CPR = 16 (256-byte rows),
@@ -130,13 +131,25 @@ __device__ __forceinline__ void dma16(const void* g, char* lds_base) {
 // corner).  The block-table entries the workgroup needs are staged in LDS
 // once; each DMA row then finds its page there.  With pos0 = 0 and dense
 // K/V this is the plain prefill.
+//
+// kMode == kAppendMode: the chunked prefill whose chunk keys and values
+// (positions pos0 .. pos0 + T - 1) arrive as dense tensors kn, vn [B, Hkv,
+// T, D] and are not yet in the cache.  Tiles take keys below pos0 from the
+// pages and the chunk's keys from kn / vn, so no workgroup waits for
+// another's writes; at its end each workgroup copies its own query block's
+// rows of kn / vn (its kv head) into their page slots through kw / vw, the
+// writable views of the pools.  Every chunk row is written once, by the
+// workgroup whose query block holds it, and read from the pools by no
+// workgroup of this launch.
 template <int D, bool kPosScale, int kMode>
 __global__ __launch_bounds__(512, 1) void prefill_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                                                               const bf16* __restrict__ v, bf16* __restrict__ out,
                                                               float* __restrict__ lse, int B, int Hq, int Hkv, int T,
                                                               int G, int BMt, int nqb, float c1,
                                                               const int* __restrict__ block_table,
-                                                              const int* __restrict__ seq_lens, int W) {
+                                                              const int* __restrict__ seq_lens, int W,
+                                                              const bf16* __restrict__ kn, const bf16* __restrict__ vn,
+                                                              bf16* kw, bf16* vw) {
     constexpr int CPR = D / 8;            // 16-byte chunks per key row
     constexpr int ROWB = D * 2;           // bytes per key row (no padding: rows are swizzled)
     constexpr int TILEB = kBN * ROWB;     // bytes per K or V tile
@@ -157,7 +170,9 @@ __global__ __launch_bounds__(512, 1) void prefill_bf16_kernel(const bf16* __rest
     // compiler wait for all LDS reads at every LDS wait inside the loop,
     // because scalar loads can complete out of order.
     __asm__ volatile("" ::"s"(q), "s"(k), "s"(v), "s"(out), "s"(lse), "s"(block_table), "s"(seq_lens));
-    constexpr bool kPaged = kMode == kPagedMode;
+    if constexpr (kMode == kAppendMode) __asm__ volatile("" ::"s"(kn), "s"(vn), "s"(kw), "s"(vw));
+    constexpr bool kAppend = kMode == kAppendMode;
+    constexpr bool kPaged = kMode == kPagedMode || kAppend;
     constexpr bool kVarlen = kMode == kVarlenMode;
     __shared__ int bt_lds[kPaged ? kMaxTablePages : 1];  // the sequence's block table (paged form)
 
@@ -293,26 +308,68 @@ __global__ __launch_bounds__(512, 1) void prefill_bf16_kernel(const bf16* __rest
     // row of the workgroup (their positions are below kend), and V is
     // finite, so they add exact zeros.  The paged form must not go past
     // kend - 1: only the block-table entries of keys 0..kend-1 are staged.
-    auto dma_tile = [&](const bf16* base, char* dst, int k0) __attribute__((always_inline)) {
+    // Append form: this (sequence, kv head)'s rows of the chunk's dense keys
+    // and values, and whether key `key` comes from them (key >= pos0) or
+    // from the pages.
+    const bf16* knb = kAppend ? kn + (size_t)(b * Hkv + kvh) * T * D : nullptr;
+    const bf16* vnb = kAppend ? vn + (size_t)(b * Hkv + kvh) * T * D : nullptr;
+    auto dma_tile = [&](const bf16* base, const bf16* dense, char* dst, int k0) __attribute__((always_inline)) {
         if constexpr (kPaged) {
-            // (page, kv head) slices are kPage rows of ROWB bytes, Hkv slices per page.
+            // (page, kv head) slices are kPage rows of ROWB bytes, Hkv slices
+            // per page; poff[j] holds the lane's row within the slice.
             const char* bb = reinterpret_cast<const char*>(base);
+            const char* db = reinterpret_cast<const char*>(dense);
             if (k0 + kBN <= kend) {
                 // A whole tile: the RPI rows of one wave-wide DMA lie in one
                 // page, so its page id is wave-uniform and the slice address
-                // is scalar work; each lane adds its fixed offset in the slice.
+                // is scalar work; each lane adds its fixed offset poff[j].
+                // The page ids of all the wave's DMAs are read from LDS
+                // before the first DMA is issued (the DMAs are asm with a
+                // memory clobber, so a read placed after one waits alone).
+                int pg[NDW];
 #pragma unroll
-                for (int j = 0; j < NDW; ++j) {
-                    const int pg = __builtin_amdgcn_readfirstlane(bt_lds[(k0 + RPI * dslot[j]) / kPage]);
-                    dma16(bb + (size_t)pg * (size_t)(Hkv * kPage * ROWB) + poff[j], dst + 1024 * dslot[j]);
+                for (int j = 0; j < NDW; ++j) pg[j] = bt_lds[(k0 + RPI * dslot[j]) / kPage];
+                auto pool_src = [&](int j) __attribute__((always_inline)) {
+                    return bb + (size_t)__builtin_amdgcn_readfirstlane(pg[j]) * (size_t)(Hkv * kPage * ROWB);
+                };
+                if (!kAppend || k0 + kBN <= pos0) {
+#pragma unroll
+                    for (int j = 0; j < NDW; ++j) dma16(pool_src(j) + poff[j], dst + 1024 * dslot[j]);
+                } else {
+                    // Append form, a tile that reaches pos0 (the chunk's own
+                    // keys): rows of the chunk are contiguous in the dense
+                    // tensor and poff[j] offsets them the same way from a
+                    // scalar base.  In the one tile that straddles pos0 each
+                    // lane picks its base.
+                    auto dense_src = [&](int j) __attribute__((always_inline)) {
+                        const int r0 = k0 + RPI * dslot[j];  // the DMA's first row (key)
+                        return db + (ptrdiff_t)(r0 - pos0 - r0 % kPage) * ROWB;
+                    };
+                    if (k0 >= pos0) {
+#pragma unroll
+                        for (int j = 0; j < NDW; ++j) dma16(dense_src(j) + poff[j], dst + 1024 * dslot[j]);
+                    } else {
+#pragma unroll
+                        for (int j = 0; j < NDW; ++j) {
+                            const int r0 = k0 + RPI * dslot[j];
+                            const char* src = lane / CPR >= pos0 - r0 ? dense_src(j) : pool_src(j);
+                            dma16(src + poff[j], dst + 1024 * dslot[j]);
+                        }
+                    }
                 }
             } else {
+                // The last tile: keys at or past kend read key kend - 1;
+                // each lane finds its own page.
 #pragma unroll
                 for (int j = 0; j < NDW; ++j) {
                     const int key = min(k0 + drow[j], kend - 1);
-                    const size_t page = (size_t)bt_lds[key / kPage];
-                    dma16(bb + (page * Hkv * kPage + key % kPage) * ROWB + (doff[j] - (uint32_t)(drow[j] * ROWB)),
-                          dst + 1024 * dslot[j]);
+                    const uint32_t chunk = poff[j] - (uint32_t)((drow[j] % kPage) * ROWB);
+                    const char* src;
+                    if (kAppend && key >= pos0)
+                        src = db + (size_t)(key - pos0) * ROWB + chunk;
+                    else
+                        src = bb + ((size_t)bt_lds[key / kPage] * Hkv * kPage + key % kPage) * ROWB + chunk;
+                    dma16(src, dst + 1024 * dslot[j]);
                 }
             }
         } else if (k0 + kBN <= Tb) {
@@ -523,7 +580,7 @@ __global__ __launch_bounds__(512, 1) void prefill_bf16_kernel(const bf16* __rest
         for (int i = tid; i < need; i += 512) bt_lds[i] = row[i];
         __syncthreads();
     }
-    if (grp == 0) dma_tile(kbase, Ks0, 0);
+    if (grp == 0) dma_tile(kbase, knb, Ks0, 0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (grp == 1) __syncthreads();
@@ -535,8 +592,8 @@ __global__ __launch_bounds__(512, 1) void prefill_bf16_kernel(const bf16* __rest
         // ---- phase 1
         mfma_phase(t > 0, Vprev, t < ntiles, Kc);
         if (grp == 0) {  // the whole tile pair, while group B finishes its softmax
-            if (t + 1 < ntiles) dma_tile(kbase, Knext, (t + 1) * kBN);
-            if (t < ntiles) dma_tile(vbase, Vcur, t * kBN);
+            if (t + 1 < ntiles) dma_tile(kbase, knb, Knext, (t + 1) * kBN);
+            if (t < ntiles) dma_tile(vbase, vnb, Vcur, t * kBN);
         }
         __syncthreads();
         // ---- phase 2
@@ -570,11 +627,43 @@ __global__ __launch_bounds__(512, 1) void prefill_bf16_kernel(const bf16* __rest
         if (lse != nullptr && hi == 0)
             lse[kVarlen ? (tok0 + token) * Hq + head : (size_t)(b * Hq + head) * T + token] = (m_run + log2f(lt)) * kLn2;
     }
+
+    // Append form: this query block's chunk rows of kv head kvh go to their
+    // page slots (positions pos0 + t0 .. kend - 1, whose block-table entries
+    // are staged).  Four 16-byte chunks per lane per round, loads first.
+    // (Reading the rows back from the last two LDS tiles instead, where they
+    // still are when a block has at most kBN rows, measured no faster.)
+    if constexpr (kAppend) {
+        const int first = pos0 + t0;         // position of the block's first row
+        const int n = (kend - first) * CPR;  // 16-byte chunks per tensor
+        auto copy_rows = [&](const bf16* src, bf16* dst) __attribute__((always_inline)) {
+            for (int i0 = 0; i0 < n; i0 += 4 * 512) {
+                bf16x8 val[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int i = i0 + 512 * u + tid;
+                    if (i < n) val[u] = *reinterpret_cast<const bf16x8*>(src + (size_t)(t0 + i / CPR) * D + 8 * (i % CPR));
+                }
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int i = i0 + 512 * u + tid;
+                    if (i < n) {
+                        const int pos = first + i / CPR;
+                        const size_t slot = ((size_t)bt_lds[pos / kPage] * Hkv + kvh) * kPage + pos % kPage;
+                        *reinterpret_cast<bf16x8*>(dst + slot * D + 8 * (i % CPR)) = val[u];
+                    }
+                }
+            }
+        };
+        copy_rows(knb, kw);
+        copy_rows(vnb, vw);
+    }
 }
 
 template <int D, int kMode>
 hipError_t launch_d(const PrefillArgs& a, const int* block_table, const int* seq_lens, int W, hipStream_t stream,
-                    int total_tokens = 0) {
+                    int total_tokens = 0, const bf16* kn = nullptr, const bf16* vn = nullptr, bf16* kw = nullptr,
+                    bf16* vw = nullptr) {
     const int G = a.Hq / a.Hkv;
     const int BMt = kRows / G;
     // Query blocks per (sequence, kv head) pair; in the packed form, a bound
@@ -586,11 +675,11 @@ hipError_t launch_d(const PrefillArgs& a, const int* block_table, const int* seq
     if (c1 > 0.f) {
         hipLaunchKernelGGL((prefill_bf16_kernel<D, true, kMode>), grid, dim3(512), 0, stream, (const bf16*)a.q,
                            (const bf16*)a.k, (const bf16*)a.v, (bf16*)a.out, a.lse, a.B, a.Hq, a.Hkv, a.T, G, BMt,
-                           nqb, c1, block_table, seq_lens, W);
+                           nqb, c1, block_table, seq_lens, W, kn, vn, kw, vw);
     } else {
         hipLaunchKernelGGL((prefill_bf16_kernel<D, false, kMode>), grid, dim3(512), 0, stream, (const bf16*)a.q,
                            (const bf16*)a.k, (const bf16*)a.v, (bf16*)a.out, a.lse, a.B, a.Hq, a.Hkv, a.T, G, BMt,
-                           nqb, c1, block_table, seq_lens, W);
+                           nqb, c1, block_table, seq_lens, W, kn, vn, kw, vw);
     }
     return hipGetLastError();
 }
@@ -612,6 +701,17 @@ hipError_t launch_prefill_varlen_bf16(const PrefillArgs& a, const int32_t* cu_se
                                       hipStream_t stream) {
     return a.d == 128 ? launch_d<128, kVarlenMode>(a, nullptr, cu_seqlens, 0, stream, total_tokens)
                       : launch_d<64, kVarlenMode>(a, nullptr, cu_seqlens, 0, stream, total_tokens);
+}
+
+hipError_t launch_prefill_paged_append_bf16(const PrefillArgs& a, const void* k_new, const void* v_new, void* k_pages,
+                                            void* v_pages, const int32_t* block_table, const int32_t* seq_lens, int W,
+                                            hipStream_t stream) {
+    const bf16* kn = static_cast<const bf16*>(k_new);
+    const bf16* vn = static_cast<const bf16*>(v_new);
+    bf16* kw = static_cast<bf16*>(k_pages);
+    bf16* vw = static_cast<bf16*>(v_pages);
+    return a.d == 128 ? launch_d<128, kAppendMode>(a, block_table, seq_lens, W, stream, 0, kn, vn, kw, vw)
+                      : launch_d<64, kAppendMode>(a, block_table, seq_lens, W, stream, 0, kn, vn, kw, vw);
 }
 
 }  // namespace attn

@@ -130,6 +130,10 @@ WORKLOADS[6] = {"chunk": ChunkShape(4, 32, 8, 2048, 128, PAGE_SIZE, 4096, 16384,
 # KV append (seed 7): the 2048-token chunks of workload 6's shape written into the paged cache.
 WORKLOADS[7] = {"append": ChunkShape(4, 32, 8, 2048, 128, PAGE_SIZE, 4096, 16384, torch.bfloat16)}
 
+# KV append fused with the chunked prefill (seed 11): workload 6's shape, the chunk's keys and values
+# arriving as dense tensors instead of already cached.
+WORKLOADS[11] = {"fused": ChunkShape(4, 32, 8, 2048, 128, PAGE_SIZE, 4096, 16384, torch.bfloat16)}
+
 # Ragged prefill (seed 8): 16 sequences of 256..4096 tokens packed along the token axis.
 WORKLOADS[8] = {"varlen": VarlenShape(16, 32, 8, 128, 256, 4096, torch.bfloat16)}
 
@@ -150,6 +154,7 @@ WORKLOAD_NAMES = {
     8: "ragged prefill bf16 over packed tokens S16 Hq32 Hkv8 d128 T~U[256,4096]",
     9: "paged decode over an FP8 E4M3 cache B64 Hq32 Hkv8 d128 page16 L~U[1024,8192]",
     10: "paged decode bf16 serving batch B1024 Hq32 Hkv8 d128 page16 L~U[16,512]",
+    11: "KV append + chunked prefill bf16 in one launch B4 Hq32 Hkv8 Tq2048 d128 page16 L~U[4096,16384]",
 }
 
 
@@ -306,6 +311,43 @@ def append_inputs(shape: ChunkShape, seed: int, *, seq_lens=None, poison=None):
     k_new = torch.randn(B, shape.Hkv, shape.Tq, shape.d, generator=g).to(shape.dtype)
     v_new = torch.randn(B, shape.Hkv, shape.Tq, shape.d, generator=g).to(shape.dtype)
     return AppendInputs(k_new, v_new, k_pages, v_pages, table, seq_lens.to(torch.int32), shape.page_size)
+
+
+@dataclass
+class FusedInputs:
+    q: torch.Tensor            # [B, Hq, Tq, d]
+    k_new: torch.Tensor        # [B, Hkv, Tq, d]: the chunk's keys
+    v_new: torch.Tensor        # [B, Hkv, Tq, d]: the chunk's values
+    k_pages: torch.Tensor      # [num_pages, Hkv, page_size, d]
+    v_pages: torch.Tensor      # [num_pages, Hkv, page_size, d]
+    block_table: torch.Tensor  # [B, W] int32, unused entries -1
+    seq_lens: torch.Tensor     # [B] int32, lengths after the append (>= Tq)
+    page_size: int
+
+
+def chunk_slots(block_table, seq_lens, Tq, page_size):
+    """(pages, slots) of the last Tq positions of every sequence, sequence-major, position order."""
+    pages, slots = [], []
+    for b, L in enumerate(seq_lens.tolist()):
+        pos = torch.arange(L - Tq, L)
+        pages.append(block_table[b].long()[pos // page_size])
+        slots.append(pos % page_size)
+    return torch.cat(pages), torch.cat(slots)
+
+
+def fused_inputs(shape: ChunkShape, seed: int, *, seq_lens=None, poison=None, stale=None):
+    """Inputs of the KV append fused with the chunked prefill: append_inputs(shape, seed, ...) (pools,
+    table, lengths, the chunk's k_new / v_new), then q [B, Hq, Tq, d] from a generator seeded
+    seed + 1000000.  ``stale``, if given, fills the chunk's own slots of the pools (values the
+    fused call overwrites and must never read)."""
+    a = append_inputs(shape, seed, seq_lens=seq_lens, poison=poison)
+    g = torch.Generator().manual_seed(seed + 1000000)
+    q = torch.randn(shape.B, shape.Hq, shape.Tq, shape.d, generator=g).to(shape.dtype)
+    if stale is not None:
+        pages, slots = chunk_slots(a.block_table, a.seq_lens, shape.Tq, a.page_size)
+        a.k_pages[pages, :, slots] = stale
+        a.v_pages[pages, :, slots] = stale
+    return FusedInputs(q, a.k_new, a.v_new, a.k_pages, a.v_pages, a.block_table, a.seq_lens, a.page_size)
 
 
 @dataclass

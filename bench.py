@@ -31,7 +31,7 @@ its clock), except where the host issues a step more slowly than the GPU
 runs it.  ``environment`` names the GPU, ROCm and torch, and the GFX clock
 amdsmi reports while the dominant kernel runs.
 
-    python bench.py [--steps K] [--warmup W] [--workload 5|3|4|6|7|8|9|10] [--no-cpu-baseline] [--flush]
+    python bench.py [--steps K] [--warmup W] [--workload 5|3|4|6|7|8|9|10|11] [--no-cpu-baseline] [--flush]
 
 ``--flush`` reads a 512 MiB buffer before every step (outside the events),
 so that a decode whose K/V would fit in the 256 MB MALL (workload 4) starts
@@ -39,7 +39,9 @@ cold; ``value`` then comes from the kernels' event time.
 
 Workload 6 (not the default) times the chunked prefill over a paged cache:
 2048-token chunks at the end of four sequences of 4096..16384 cached tokens.
-Workload 7 times the KV append that writes such chunks into the cache.
+Workload 7 times the KV append that writes such chunks into the cache, and
+workload 11 the two in one launch (the chunk's keys and values arriving as
+dense tensors, read from there and written into the cache by the prefill).
 Workload 8 times the ragged prefill of 16 sequences of 256..4096 tokens
 packed along the token axis.  Workload 9 times the paged decode of workload
 5 over an FP8 E4M3 cache (algorithmic bytes: one byte per cached value).
@@ -169,7 +171,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workload", type=int, default=5, choices=(3, 4, 5, 6, 7, 8, 9, 10))
+    p.add_argument("--workload", type=int, default=5, choices=(3, 4, 5, 6, 7, 8, 9, 10, 11))
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--sequential", action="store_true",
                    help="run the parts of a two-part step (workload 5) one after the other on one stream; by default "
@@ -380,6 +382,37 @@ def cpu_baseline_chunk(inp, budget_s=20.0):
             "chunk_tflops": flops / t / 1e12, "host_cpu_count": os.cpu_count()}
 
 
+def cpu_baseline_fused(inp, budget_s=20.0):
+    """Time the fp64 oracle on a bounded sample of the fused workload: sequence 0, query head by query
+    head, each call appending that head's kv-head slice of the chunk and attending over the result."""
+    import oracle
+    from threadpoolctl import threadpool_info
+
+    threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    B, Hq, Tq, d = inp.q.shape
+    Hkv = inp.k_pages.shape[1]
+    g = Hq // Hkv
+    kp, vp = inp.k_pages.float().numpy(), inp.v_pages.float().numpy()
+    kn, vn = inp.k_new.float().numpy(), inp.v_new.float().numpy()
+    L = int(inp.seq_lens[0])
+    scale = synth.fp32_scale(d)
+    t0 = time.perf_counter()
+    heads = 0
+    while heads < Hq and (heads == 0 or time.perf_counter() - t0 < budget_s):
+        h, kv = heads, heads // g
+        oracle.prefill_paged_append(inp.q[0:1, h:h + 1].float().numpy(), kn[0:1, kv:kv + 1], vn[0:1, kv:kv + 1],
+                                    kp[:, kv:kv + 1], vp[:, kv:kv + 1], inp.block_table[0:1].numpy(),
+                                    inp.seq_lens[0:1].numpy(), scale, inp.page_size)
+        heads += 1
+    t = time.perf_counter() - t0
+    flops = heads * synth.chunk_flops(1, d, Tq, [L])
+    return {"value": flops / t / PEAK_BF16_FLOPS, "unit": "fraction of MI355X roofline", "cores": threads,
+            "kind": "oracle",
+            "sample": f"fp64 oracle: KV append + chunked prefill of sequence 0 (L={L}), {heads} of {Hq} query heads "
+                      f"({t:.2f} s)",
+            "chunk_tflops": flops / t / 1e12, "host_cpu_count": os.cpu_count()}
+
+
 def cpu_baseline_append(inp):
     """Time the oracle's KV append on the whole workload (bf16 values moved as 16-bit patterns)."""
     import oracle
@@ -469,8 +502,9 @@ def main():
     app_shape = wl.get("append")
     var_shape = wl.get("varlen")
     f8_shape = wl.get("decode_fp8")
+    fu_shape = wl.get("fused")
 
-    pre_inputs = dec_inputs = chunk_in = app_in = var_in = f8_in = None
+    pre_inputs = dec_inputs = chunk_in = app_in = var_in = f8_in = fu_in = None
     work = {}
     if pre_shape is not None:
         pre_inputs = synth.prefill_inputs(pre_shape, seed=args.workload)
@@ -505,6 +539,18 @@ def main():
         akn, avn, akp, avp, abt, asl = (t.to(dev) for t in (app_in.k_new, app_in.v_new, app_in.k_pages,
                                                             app_in.v_pages, app_in.block_table, app_in.seq_lens))
         work["append"] = lambda: A.attn_kv_append(akn, avn, akp, avp, abt, asl)
+    if fu_shape is not None:
+        # The launch rewrites the chunk's slots with the same values at every
+        # step, and reads the chunk's keys from k_new / v_new: steps repeat
+        # exactly.
+        fu_in = synth.fused_inputs(fu_shape, seed=args.workload)
+        uq, ukn, uvn, ukp, uvp, ubt, usl = (t.to(dev) for t in (fu_in.q, fu_in.k_new, fu_in.v_new, fu_in.k_pages,
+                                                                fu_in.v_pages, fu_in.block_table, fu_in.seq_lens))
+        uout = torch.empty_like(uq)
+        ulse = torch.empty(uq.shape[:3], dtype=torch.float32, device=dev)
+        uscale = synth.fp32_scale(fu_shape.d)
+        work["fused"] = lambda: A.attn_prefill_paged_append(uq, ukn, uvn, ukp, uvp, ubt, usl, out=uout, lse=ulse,
+                                                            scale=uscale)
     if var_shape is not None:
         var_in = synth.varlen_inputs(var_shape, seed=args.workload)
         vq, vk, vv, vcu = (t.to(dev) for t in var_in[:4])
@@ -751,6 +797,14 @@ def main():
         parts["chunk"] = {"ms": round(ms["chunk"], 4), **spread("chunk"),
                           "tflops": round(flops / t / 1e12, 1), "frac_of_peak": round(flops / t / PEAK_BF16_FLOPS, 4),
                           "flops_per_launch": flops}
+    if fu_shape is not None:
+        flops = synth.chunk_flops(fu_shape.Hq, fu_shape.d, fu_shape.Tq, fu_in.seq_lens.tolist())
+        t = ms["fused"] / 1e3
+        at_peak += flops / PEAK_BF16_FLOPS
+        parts["fused"] = {"ms": round(ms["fused"], 4), **spread("fused"),
+                          "tflops": round(flops / t / 1e12, 1), "frac_of_peak": round(flops / t / PEAK_BF16_FLOPS, 4),
+                          "flops_per_launch": flops,
+                          "append_bytes_per_launch": 2 * fu_in.k_new.numel() * fu_in.k_new.element_size()}
     if var_shape is not None:
         lens = (var_in[3][1:] - var_in[3][:-1]).tolist()
         flops = synth.varlen_flops(var_shape.Hq, var_shape.d, lens)
@@ -784,9 +838,9 @@ def main():
 
     # Dominant kernel's roofline (the one with the larger share of the step).
     dom = max(names, key=lambda n: ms[n])
-    if dom in ("prefill", "chunk", "varlen"):
+    if dom in ("prefill", "chunk", "varlen", "fused"):
         src = kernel_source_hash(["prefill_bf16.hip", "device_common.h"])
-        form = {"prefill": "", "chunk": " (paged form)", "varlen": " (packed form)"}[dom]
+        form = {"prefill": "", "chunk": " (paged form)", "varlen": " (packed form)", "fused": " (append form)"}[dom]
         roof = {"kernel": "prefill_bf16_kernel" + form, "bound": "mfma",
                 "achieved": parts[dom]["tflops"], "peak": PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s",
                 "frac": round(parts[dom]["tflops"] * 1e12 / PEAK_BF16_FLOPS, 4),
@@ -841,6 +895,9 @@ def main():
     if chunk_in is not None:
         cfg["seed_chunk"] = args.workload
         cfg["chunk_seq_lens"] = chunk_in.seq_lens.tolist()
+    if fu_in is not None:
+        cfg["seed_fused"] = args.workload
+        cfg["fused_seq_lens"] = fu_in.seq_lens.tolist()
     result.update({
         "value": round(value, 4),
         "unit": "fraction of MI355X roofline (step time at peak / measured step time)",
@@ -875,6 +932,8 @@ def main():
         result["cpu_baseline"] = cpu_baseline_chunk(chunk_in)
     if not args.no_cpu_baseline and args.workload == 7:
         result["cpu_baseline"] = cpu_baseline_append(app_in)
+    if not args.no_cpu_baseline and args.workload == 11:
+        result["cpu_baseline"] = cpu_baseline_fused(fu_in)
     if not args.no_cpu_baseline and args.workload == 9:
         result["cpu_baseline"] = cpu_baseline_fp8(f8_in)
     if not args.no_cpu_baseline and args.workload == 8:

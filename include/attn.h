@@ -1,7 +1,7 @@
 /*
  * attn.h — causal multi-head / grouped-query attention for MI355X (gfx950).
  *
- * Six operations, all hand-written HIP kernels behind a plain C ABI:
+ * Seven operations, all hand-written HIP kernels behind a plain C ABI:
  *
  *  - attn_prefill: causal self-attention of T queries over the same T keys,
  *    computed block by block with an online softmax so that the T x T score
@@ -39,6 +39,12 @@
  *    slots of the paged cache (the KV-cache writer of the RoseLLM README,
  *    "Systems highlights", "Inference and serving"), the step before decode
  *    or chunked prefill reads them.
+ *
+ *  - attn_prefill_paged_append: KV append and chunked prefill in one launch:
+ *    the chunk's keys and values arrive as dense tensors, the attention reads
+ *    them from there (and the older keys from the pages), and the same
+ *    launch writes them into their page slots.  Same results as
+ *    attn_kv_append followed by attn_prefill_paged, bit for bit.
  *
  * What is computed.  For query head h, the kv head read is h / (Hq / Hkv)
  * (consecutive groups of query heads share one kv head).  For a query q and
@@ -190,6 +196,44 @@ int attn_kv_append(const void* k_new, const void* v_new, void* k_pages, void* v_
                    const int32_t* block_table, const int32_t* seq_lens,
                    int B, int Hkv, int Tn, int d, int page_size, int num_pages,
                    int max_pages_per_seq, int dtype, hipStream_t stream);
+
+/*
+ * Fused KV append + chunked prefill: the work of attn_kv_append(k_new, v_new,
+ * k_pages, v_pages, ...) followed by attn_prefill_paged(q, k_pages, v_pages,
+ * ...) with the same sizes, in one launch; out, lse and the pools come out
+ * bit for bit as from those two calls.
+ *
+ *   q, out         : device, [B, Hq, Tq, d]; row t of sequence b is the query
+ *                    at position seq_lens[b] - Tq + t
+ *   k_new, v_new   : device, [B, Hkv, Tq, d]: the chunk's keys and values,
+ *                    token t at position seq_lens[b] - Tq + t
+ *   k_pages,v_pages: device, [num_pages, Hkv, page_size, d]; read for the
+ *                    positions below seq_lens[b] - Tq, written (bit-exact
+ *                    copies of k_new / v_new) at the chunk's positions; no
+ *                    other byte changes
+ *   block_table    : device int32 [B, max_pages_per_seq], as for decode
+ *   seq_lens       : device int32 [B]; lengths after the append, each in
+ *                    [Tq, max_pages_per_seq * page_size]
+ *   lse            : device float32 [B, Hq, Tq], or NULL to skip it
+ *   B, Tq          : >= 0 (either 0 enqueues nothing and returns ATTN_OK)
+ *   Hq, Hkv        : >= 1, Hq % Hkv == 0, Hq / Hkv <= 128
+ *   dtype          : ATTN_BF16; d = 128 or 64; page_size = 16;
+ *                    max_pages_per_seq <= 8192
+ * Within the launch no (page, slot) is both written and read: the chunk's
+ * keys are read from k_new / v_new only.  So, beyond the conditions of the
+ * two calls it replaces (two chunk tokens must not name the same (page,
+ * slot)), a slot written for one sequence must not be a slot that another
+ * sequence of the batch reads as part of its cached prefix.  q, k_new, v_new
+ * and the cached prefix must hold finite values.  Metadata is read on the
+ * device only (check it with attn_validate_chunk_metadata, chunk_len = Tq).
+ */
+int attn_prefill_paged_append(const void* q, const void* k_new, const void* v_new,
+                              void* k_pages, void* v_pages,
+                              const int32_t* block_table, const int32_t* seq_lens,
+                              void* out, float* lse,
+                              int B, int Hq, int Hkv, int Tq, int d, int page_size, int num_pages,
+                              int max_pages_per_seq, float scale, int dtype,
+                              hipStream_t stream);
 
 /*
  * Split plan of attn_decode_paged: a sequence's page list may be cut only at

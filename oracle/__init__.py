@@ -30,6 +30,7 @@ from .attention import (  # noqa: F401
     kv_head_of,
     prefill,
     prefill_paged,
+    prefill_paged_append,
     prefill_varlen,
     prefill_rows,
 )

@@ -256,6 +256,21 @@ def kv_append(k_pages, v_pages, k_new, v_new, block_table, seq_lens, page_size):
     return k_out, v_out
 
 
+def prefill_paged_append(q, k_new, v_new, k_pages, v_pages, block_table, seq_lens, scale, page_size, rows=None):
+    """KV append of a chunk followed by the chunked prefill of its queries.
+
+    The step of a chunked prefill in a paged-cache server (RoseLLM README,
+    "Systems highlights", "Inference and serving": the KV-cache writer, then
+    chunked prefill over the paged cache): the chunk's keys and values
+    k_new / v_new [B, Hkv, Tq, d] are written into their slots (kv_append),
+    then the chunk's queries q [B, Hq, Tq, d] attend over the updated cache
+    (prefill_paged).  Returns (out, lse, k_pages after, v_pages after).
+    """
+    k_after, v_after = kv_append(k_pages, v_pages, k_new, v_new, block_table, seq_lens, page_size)
+    out, lse = prefill_paged(q, k_after, v_after, block_table, seq_lens, scale, page_size, rows=rows)
+    return out, lse, k_after, v_after
+
+
 def prefill_varlen(q, k, v, cu_seqlens, scale):
     """Causal prefill of a ragged batch packed along the token axis.
 

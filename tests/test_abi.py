@@ -27,7 +27,8 @@ def declared_functions():
 
 def test_header_declares_the_api():
     names = declared_functions()
-    for n in ("attn_prefill", "attn_prefill_paged", "attn_prefill_varlen", "attn_validate_varlen_metadata",
+    for n in ("attn_prefill", "attn_prefill_paged", "attn_prefill_paged_append", "attn_prefill_varlen",
+              "attn_validate_varlen_metadata",
               "attn_kv_append", "attn_decode_paged_fp8", "attn_decode_paged", "attn_decode_workspace_bytes",
               "attn_decode_num_splits", "attn_validate_paged_metadata", "attn_validate_chunk_metadata",
               "attn_status_string", "attn_last_error_message"):
@@ -222,6 +223,53 @@ def test_prefill_paged_rejects(lib, kw, status):
 def test_prefill_paged_empty_is_a_no_op(lib):
     assert prefill_paged(lib, q=None, kp=None, vp=None, bt=None, sl=None, out=None, B=0) == A.ATTN_OK
     assert prefill_paged(lib, q=None, kp=None, vp=None, bt=None, sl=None, out=None, Tq=0) == A.ATTN_OK
+
+
+def prefill_paged_append(lib, q=FAKE, kn=FAKE, vn=FAKE, kp=FAKE, vp=FAKE, bt=FAKE, sl=FAKE, out=FAKE, lse=None, B=2,
+                         Hq=4, Hkv=2, Tq=40, d=128, ps=16, P=10, W=8, scale=0.1, dtype=1):
+    return lib.attn_prefill_paged_append(q, kn, vn, kp, vp, bt, sl, out, lse, B, Hq, Hkv, Tq, d, ps, P, W, scale, dtype,
+                                         None)
+
+
+@pytest.mark.parametrize(
+    "kw,status",
+    [
+        (dict(q=None), A.ATTN_ERR_INVALID_ARG),
+        (dict(kn=None), A.ATTN_ERR_INVALID_ARG),
+        (dict(vn=None), A.ATTN_ERR_INVALID_ARG),
+        (dict(kp=None), A.ATTN_ERR_INVALID_ARG),
+        (dict(vp=None), A.ATTN_ERR_INVALID_ARG),
+        (dict(bt=None), A.ATTN_ERR_INVALID_ARG),
+        (dict(sl=None), A.ATTN_ERR_INVALID_ARG),
+        (dict(out=None), A.ATTN_ERR_INVALID_ARG),
+        (dict(vn=FAKE + 8), A.ATTN_ERR_INVALID_ARG),
+        (dict(vp=FAKE + 4), A.ATTN_ERR_INVALID_ARG),
+        (dict(bt=FAKE + 2), A.ATTN_ERR_INVALID_ARG),
+        (dict(lse=FAKE + 1), A.ATTN_ERR_INVALID_ARG),
+        (dict(Hq=5, Hkv=2), A.ATTN_ERR_INVALID_ARG),
+        (dict(B=-1), A.ATTN_ERR_INVALID_ARG),
+        (dict(Tq=-1), A.ATTN_ERR_INVALID_ARG),
+        (dict(Tq=8 * 16 + 1), A.ATTN_ERR_INVALID_ARG),
+        (dict(W=0), A.ATTN_ERR_INVALID_ARG),
+        (dict(P=-1), A.ATTN_ERR_INVALID_ARG),
+        (dict(scale=float("nan")), A.ATTN_ERR_INVALID_ARG),
+        (dict(dtype=5), A.ATTN_ERR_INVALID_ARG),
+        (dict(dtype=0), A.ATTN_ERR_UNSUPPORTED),
+        (dict(d=96), A.ATTN_ERR_UNSUPPORTED),
+        (dict(ps=32, Tq=40), A.ATTN_ERR_UNSUPPORTED),
+        (dict(Hq=256, Hkv=1), A.ATTN_ERR_UNSUPPORTED),
+        (dict(W=8193), A.ATTN_ERR_UNSUPPORTED),
+    ],
+)
+def test_prefill_paged_append_rejects(lib, kw, status):
+    assert prefill_paged_append(lib, **kw) == status
+    assert A.attn_last_error_message() != ""
+
+
+def test_prefill_paged_append_empty_is_a_no_op(lib):
+    none = dict(q=None, kn=None, vn=None, kp=None, vp=None, bt=None, sl=None, out=None)
+    assert prefill_paged_append(lib, B=0, **none) == A.ATTN_OK
+    assert prefill_paged_append(lib, Tq=0, **none) == A.ATTN_OK
 
 
 def kv_append(lib, kn=FAKE, vn=FAKE, kp=FAKE, vp=FAKE, bt=FAKE, sl=FAKE, B=2, Hkv=2, Tn=40, d=128, ps=16, P=10, W=8,

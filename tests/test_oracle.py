@@ -414,6 +414,35 @@ def test_append_then_decode_equals_dense_history():
     np.testing.assert_allclose(ld, lp[:, :, L - 1], rtol=0, atol=1e-13)
 
 
+def test_fused_chunks_rebuild_a_dense_prefill():
+    """Start from an empty (NaN) cache and feed two sequences chunk by chunk through the fused append +
+    chunked prefill: each chunk's rows are the matching rows of a dense causal prefill over the whole
+    sequence, and the final cache holds every token's K/V."""
+    r = rng(43)
+    B, Hq, Hkv, d, ps, L = 2, 4, 2, 3, 4, 11
+    q = 2.0 * r.standard_normal((B, Hq, L, d))
+    k = r.standard_normal((B, Hkv, L, d))
+    v = r.standard_normal((B, Hkv, L, d))
+    W = -(-L // ps)
+    P = B * W
+    table = r.permutation(P).reshape(B, W)
+    kp = np.full((P, Hkv, ps, d), np.nan)
+    vp = np.full((P, Hkv, ps, d), np.nan)
+    od, ld = oracle.prefill(q, k, v, 0.7)
+    start = 0
+    for Tq in (3, 4, 4):
+        end = start + Tq
+        out, lse, kp, vp = oracle.prefill_paged_append(q[:, :, start:end], k[:, :, start:end], v[:, :, start:end],
+                                                       kp, vp, table, np.array([end] * B), 0.7, ps)
+        np.testing.assert_allclose(out, od[:, :, start:end], rtol=0, atol=1e-13)
+        np.testing.assert_allclose(lse, ld[:, :, start:end], rtol=0, atol=1e-13)
+        start = end
+    for b in range(B):
+        for kvh in range(Hkv):
+            np.testing.assert_array_equal(oracle.gather_pages(kp, table[b], L, ps, kvh), k[b, kvh])
+            np.testing.assert_array_equal(oracle.gather_pages(vp, table[b], L, ps, kvh), v[b, kvh])
+
+
 # ---------------------------------------------------------------- ragged (varlen) prefill
 def varlen_case(seed, lens, Hq=4, Hkv=2, d=3):
     r = rng(seed)

@@ -71,6 +71,15 @@ MUTATIONS = {
     "fp8 sign ignored": [("sign = np.where(c & 0x80, -1.0, 1.0)", "sign = 1.0")],
     "fp8 value scale on the keys": [("vals = fp8_e4m3_value(v_codes) * float(v_scale)",
                                      "vals = fp8_e4m3_value(v_codes) * float(k_scale)")],
+    "fused step attends before appending": [
+        ("    k_after, v_after = kv_append(k_pages, v_pages, k_new, v_new, block_table, seq_lens, page_size)\n"
+         "    out, lse = prefill_paged(q, k_after, v_after,",
+         "    out, lse = prefill_paged(q, k_pages, v_pages,"),
+        ("page_size, rows=rows)\n    return out, lse, k_after, v_after",
+         "page_size, rows=rows)\n    k_after, v_after = kv_append(k_pages, v_pages, k_new, v_new, block_table, "
+         "seq_lens, page_size)\n    return out, lse, k_after, v_after"),
+    ],
+    "fused step returns the old cache": [("    return out, lse, k_after, v_after", "    return out, lse, k_pages, v_pages")],
     "append writes V into K": [("k_out[page, :, position % page_size] = np.asarray(k_new)[b, :, t]",
                                 "k_out[page, :, position % page_size] = np.asarray(v_new)[b, :, t]")],
 }
