@@ -45,3 +45,41 @@ def test_prefill_and_decode_graph_replays_match_eager():
         torch.cuda.synchronize()
         for name, got, want in zip(("out", "lse", "dout", "dlse"), (out, lse, dout, dlse), ref):
             assert torch.equal(got, want), f"replay {r}: {name} differs from the eager launch"
+
+
+def test_fused_append_graph_replays_rewrite_the_cache():
+    """The fused append + chunked prefill under capture: before every replay the chunk's slots are set back
+    to NaN and the outputs cleared, and every replay must write the same slots and outputs as the eager call."""
+    dev = device()
+    shp = synth.ChunkShape(3, 8, 2, 100, 128, synth.PAGE_SIZE, 100, 700, torch.bfloat16)
+    inp = synth.fused_inputs(shp, seed=23, poison=float("nan"), stale=float("nan"))
+    q, kn, vn, kp, vp, bt, sl = (t.to(dev) for t in (inp.q, inp.k_new, inp.v_new, inp.k_pages, inp.v_pages,
+                                                     inp.block_table, inp.seq_lens))
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    pages, slots = (t.to(dev) for t in synth.chunk_slots(inp.block_table, inp.seq_lens, 100, synth.PAGE_SIZE))
+    scale = synth.fp32_scale(128)
+
+    def work():
+        A.attn_prefill_paged_append(q, kn, vn, kp, vp, bt, sl, out=out, lse=lse, scale=scale)
+
+    say("[graph] fused append: eager reference")
+    work()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (out, lse, kp, vp)]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        work()
+    for r in range(4):
+        say(f"[graph] fused append: replay {r}")
+        out.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        kp[pages, :, slots] = float("nan")  # eager work between replays: the chunk's slots are stale again
+        vp[pages, :, slots] = float("nan")
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for name, got, want in zip(("out", "lse", "k_pages", "v_pages"), (out, lse, kp, vp), ref):
+            assert torch.equal(got.view(torch.int16) if got.dtype == torch.bfloat16 else got,
+                               want.view(torch.int16) if want.dtype == torch.bfloat16 else want), \
+                f"replay {r}: {name} differs from the eager launch"

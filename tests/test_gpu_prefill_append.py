@@ -173,3 +173,19 @@ def test_workload11_full():
     e = max_err(np64(o1)[:, :, rows], ref_o[:, :, rows], "w11 out", TOL_BF16)
     max_err(np64(l1)[:, :, rows], ref_l[:, :, rows], "w11 lse", TOL_LSE)
     say(f"    max err out {e:.3e}")
+
+
+def test_fused_longest_supported_context():
+    """Contexts of 131072 tokens, the whole 8192-entry block table staged in LDS; sampled rows."""
+    lens = [131072, 131072 - 5]
+    shp = synth.ChunkShape(len(lens), 8, 2, 64, 128, synth.PAGE_SIZE, 1, 131072, BF16)
+    inp = synth.fused_inputs(shp, seed=1600, seq_lens=lens, poison=NAN, stale=NAN)
+    assert inp.block_table.shape[1] == 8192
+    check(inp, synth.fp32_scale(128), "contexts of 131072 tokens (8192 pages)", rows=[0, 1, 31, 62, 63])
+
+
+def test_fused_largest_group():
+    """Hq / Hkv = 128: two chunk rows per workgroup."""
+    shp = synth.ChunkShape(2, 128, 1, 37, 64, synth.PAGE_SIZE, 37, 300, BF16)
+    inp = synth.fused_inputs(shp, seed=1700, poison=NAN, stale=NAN)
+    check(inp, synth.fp32_scale(64), "Hq128 Hkv1 d64")
