@@ -1,6 +1,6 @@
 """Causal MHA/GQA attention for MI355X (gfx950): bf16 MFMA prefill (dense, ragged over packed tokens, or
 chunked over a paged cache, alone or fused with the chunk's KV append), paged split-KV decode (bf16 or FP8 E4M3
-cache), and the paged-cache KV append.
+cache, bf16 optionally with the newest token's append fused), and the paged-cache KV append.
 
 The compute lives in ``libattn.so`` (hand-written HIP kernels behind the C ABI
 declared in ``include/attn.h``); this package is its ctypes binding, with the
@@ -20,6 +20,7 @@ from ._binding import (  # noqa: F401
     AttnError,
     attn_decode_num_splits,
     attn_decode_paged,
+    attn_decode_paged_append,
     attn_decode_paged_fp8,
     attn_decode_paged_noalloc,
     attn_decode_workspace_bytes,

@@ -53,6 +53,9 @@ def load_library():
     lib.attn_decode_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, i32, i32,
                                       vp, sz, vp]
     lib.attn_decode_paged.restype = i32
+    lib.attn_decode_paged_append.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
+                                             f32, i32, i32, vp, sz, vp]
+    lib.attn_decode_paged_append.restype = i32
     lib.attn_decode_paged_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32,
                                               i32, i32, vp]
     lib.attn_decode_paged_noalloc.restype = i32
@@ -348,6 +351,54 @@ def attn_decode_paged(q, k_pages, v_pages, block_table, seq_lens, out=None, lse=
     _check(lib.attn_decode_paged(_ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table), _ptr(seq_lens), _ptr(out),
                                  None if lse is False else _ptr(lse), B, Hq, Hkv, d, page_size, P, W, float(scale),
                                  _dtype_code(q), num_splits, _ptr(workspace), ws_bytes, _stream(stream)))
+    return out, (None if lse is False else lse)
+
+
+def attn_decode_paged_append(q, k_new, v_new, k_pages, v_pages, block_table, seq_lens, out=None, lse=None,
+                             scale=None, num_splits=0, workspace=None, stream=None):
+    """Paged single-token decode with the newest token's KV append fused.  q [B,Hq,d]; k_new/v_new [B,Hkv,d] or
+    [B,Hkv,1,d] (written into the pools in place at position seq_lens[b] - 1); pools [P,Hkv,page,d]; block_table
+    [B,W] int32; seq_lens [B] int32 = lengths after the append."""
+    torch = _torch()
+    _require(q.dim() == 3 and k_pages.dim() == 4 and k_pages.shape == v_pages.shape, "bad q / page pool shapes")
+    B, Hq, d = q.shape
+    P, Hkv, page_size, dk = k_pages.shape
+    _require(dk == d, "page pools and q disagree on d")
+    _require(k_new.shape == v_new.shape and tuple(k_new.shape) in ((B, Hkv, d), (B, Hkv, 1, d)),
+             "k_new and v_new must be [B, Hkv, d] or [B, Hkv, 1, d]")
+    _require(block_table.dim() == 2 and block_table.shape[0] == B and block_table.dtype == torch.int32,
+             "block_table must be int32 [B, W]")
+    _require(seq_lens.shape == (B,) and seq_lens.dtype == torch.int32, "seq_lens must be int32 [B]")
+    for n, t in (("q", q), ("k_new", k_new), ("v_new", v_new), ("k_pages", k_pages), ("v_pages", v_pages),
+                 ("block_table", block_table), ("seq_lens", seq_lens)):
+        _dense_on_gpu(n, t)
+    _require(q.dtype == k_new.dtype == v_new.dtype == k_pages.dtype == v_pages.dtype,
+             "q, k_new, v_new and the page pools must share a dtype")
+    W = block_table.shape[1]
+    with _alloc_stream(stream):
+        if out is None:
+            out = torch.empty_like(q)
+        if lse is None:
+            lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    _dense_on_gpu("out", out)
+    _require(out.shape == q.shape and out.dtype == q.dtype, "out must match q")
+    if lse is not False:
+        _dense_on_gpu("lse", lse)
+        _require(lse.shape == (B, Hq) and lse.dtype == torch.float32, "lse must be float32 [B, Hq]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    lib = load_library()
+    need = lib.attn_decode_workspace_bytes(B, Hq, Hkv, d, page_size, W, num_splits)
+    if workspace is None:
+        with _alloc_stream(stream):
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _dense_on_gpu("workspace", workspace)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib.attn_decode_paged_append(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_pages), _ptr(v_pages),
+                                        _ptr(block_table), _ptr(seq_lens), _ptr(out),
+                                        None if lse is False else _ptr(lse), B, Hq, Hkv, d, page_size, P, W,
+                                        float(scale), _dtype_code(q), num_splits, _ptr(workspace), ws_bytes,
+                                        _stream(stream)))
     return out, (None if lse is False else lse)
 
 

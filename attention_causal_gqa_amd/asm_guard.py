@@ -658,6 +658,11 @@ class _Analysis:
                 return out
             return [(taken, st.copy()), (fall, st.copy())]
         if cond in ("execz", "execnz"):
+            if st.exec in st.nonempty:
+                # exec is known to hold a lane on this path (for example the
+                # wave's whole mask, which the structurizer tests again after
+                # a uniform branch's arm): the execz edge cannot be taken
+                return [(fall, st.copy())] if cond == "execz" else [(taken, st.copy())]
             s_nz = st.copy()
             s_nz.nonempty = s_nz.nonempty | {st.exec}
             return [(taken, st.copy() if cond == "execz" else s_nz), (fall, s_nz if cond == "execz" else st.copy())]

@@ -408,6 +408,34 @@ int attn_decode_paged(const void* q, const void* k_pages, const void* v_pages, c
     return from_hip(attn::launch_decode_bf16(a, stream), "attn_decode_paged launch");
 }
 
+int attn_decode_paged_append(const void* q, const void* k_new, const void* v_new, void* k_pages, void* v_pages,
+                             const int32_t* block_table, const int32_t* seq_lens, void* out, float* lse, int B, int Hq,
+                             int Hkv, int d, int page_size, int num_pages, int max_pages_per_seq, float scale,
+                             int dtype, int num_splits, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    g_last_error.clear();
+    if (dtype != ATTN_F32 && dtype != ATTN_BF16) return fail(ATTN_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+    int st = check_decode_sizes(B, Hq, Hkv, d, page_size, max_pages_per_seq, num_splits);
+    if (st != ATTN_OK) return st;
+    if (num_pages < 0) return fail(ATTN_ERR_INVALID_ARG, "num_pages=%d must be >= 0", num_pages);
+    if (!std::isfinite(scale)) return fail(ATTN_ERR_INVALID_ARG, "scale must be finite");
+    if (dtype != ATTN_BF16) return fail(ATTN_ERR_UNSUPPORTED, "decode with append supports ATTN_BF16 only");
+    if (B == 0) return ATTN_OK;
+    if (!q || !k_new || !v_new || !k_pages || !v_pages || !block_table || !seq_lens || !out)
+        return fail(ATTN_ERR_INVALID_ARG,
+                    "q, k_new, v_new, k_pages, v_pages, block_table, seq_lens and out must be non-null");
+    if (!aligned(q, 16) || !aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(k_pages, 16) ||
+        !aligned(v_pages, 16) || !aligned(out, 16))
+        return fail(ATTN_ERR_INVALID_ARG, "q, k_new, v_new, k_pages, v_pages and out must be 16-byte aligned");
+    if (!aligned(block_table, 4) || !aligned(seq_lens, 4) || (lse && !aligned(lse, 4)))
+        return fail(ATTN_ERR_INVALID_ARG, "block_table, seq_lens and lse must be 4-byte aligned");
+
+    attn::DecodeArgs a{};
+    st = decode_args(q, k_pages, v_pages, block_table, seq_lens, out, lse, B, Hq, Hkv, d, page_size,
+                     max_pages_per_seq, scale, num_splits, workspace, workspace_bytes, &a);
+    if (st != ATTN_OK) return st;
+    return from_hip(attn::launch_decode_append_bf16(a, k_new, v_new, stream), "attn_decode_paged_append launch");
+}
+
 int attn_decode_paged_noalloc(const void* q, const void* k_pages, const void* v_pages, const int32_t* block_table,
                               const int32_t* seq_lens, void* out, float* lse, int B, int Hq, int Hkv, int d,
                               int page_size, int num_pages, int max_pages_per_seq, float scale, int dtype,

@@ -172,7 +172,14 @@ __device__ __forceinline__ long long wave_incl_scan(long long v, int lane) {
 //                  comes HBM -> LDS by DMA and is read transposed)
 // The next page's K and V loads are in flight while a page is computed, and
 // the block-table entry of the page after that is loaded a step earlier.
-template <int D, bool kFp8>
+//
+// Append form (kAppend): the newest token of each sequence (position L - 1)
+// is not yet in the pools; its key and value rows arrive in kn, vn
+// [B, Hkv, d].  On a run's last page the lanes that would load row
+// (L - 1) % 16 load it from there instead (same number of loads), so no
+// wave reads the slot; the combine kernel, which runs after this one,
+// writes it.
+template <int D, bool kFp8, bool kAppend>
 __global__ __launch_bounds__(64) void decode_stream_kernel(const bf16* __restrict__ q, const char* __restrict__ kp,
                                                             const char* __restrict__ vp,
                                                             const int32_t* __restrict__ block_table,
@@ -180,7 +187,9 @@ __global__ __launch_bounds__(64) void decode_stream_kernel(const bf16* __restric
                                                             bf16* __restrict__ out, float* __restrict__ lse,
                                                             float* __restrict__ o_part, float* __restrict__ lse_part,
                                                             int* __restrict__ run_info, int B, int Hq, int Hkv, int G,
-                                                            int W, int pps, float c1, float vscale) {
+                                                            int W, int pps, float c1, float vscale,
+                                                            const bf16* __restrict__ kn, const bf16* __restrict__ vn) {
+    static_assert(!(kFp8 && kAppend), "the append form reads bf16 pools");
     constexpr int NKK = D / 32;        // k-steps of QK^T (16x16x32)
     constexpr int NB = D / 16;         // 16-column blocks of O (16x16x16)
     constexpr int ROWB = D * 2;        // bytes per token row in bf16 (the LDS layout of V)
@@ -333,9 +342,33 @@ __global__ __launch_bounds__(64) void decode_stream_kernel(const bf16* __restric
     const int vrow = 4 * g + (vi >> 2);
     const int vread = vrow * ROWB + 8 * (vi & 1) + ((((vi & 3) >> 1) ^ vswz<D>(vrow)) << 4);
 
-    auto issue_page = [&](int pid, int kvh, char* vdst, KReg(&ka)[NKK]) __attribute__((always_inline)) {
+    auto issue_page = [&](int pid, const Cursor& c, char* vdst, KReg(&ka)[NKK]) __attribute__((always_inline)) {
+        const int kvh = c.kvh;
         const size_t slice = ((size_t)pid * Hkv + kvh) * KSLICEB;
         const char* kb = kp + slice;
+        if constexpr (kAppend) {
+            // Wave-uniform (the cursor is), made explicit so that the branch
+            // is a scalar one: under a vector branch the compiler would run
+            // both paths under exec masks, one after the other.
+            if (__builtin_amdgcn_readfirstlane(c.j == c.n - 1)) {
+                // The run's last page: row nrow is the new token, read from
+                // kn / vn (rows of ROWB bytes, the same chunk offsets).
+                const int nrow = __builtin_amdgcn_readfirstlane((c.L - 1) % kPage);
+                const size_t nr = ((size_t)c.b * Hkv + kvh) * ROWB;
+                const char* kr = reinterpret_cast<const char*>(kn) + nr;
+                const char* vr = reinterpret_cast<const char*>(vn) + nr;
+                const char* kl = hd == nrow ? kr + (koff - (uint32_t)(hd * KROWB)) : kb + koff;
+#pragma unroll
+                for (int kk = 0; kk < NKK; ++kk) ka[kk] = gload16(kl + 64 * kk);
+                const char* vb = vp + slice;
+#pragma unroll
+                for (int n = 0; n < NDMA; ++n) {
+                    const int row = RPD * n + lane / KCPR;
+                    dma16(row == nrow ? vr + (voff[n] - (uint32_t)(row * KROWB)) : vb + voff[n], vdst + 1024 * n);
+                }
+                return;
+            }
+        }
 #pragma unroll
         for (int kk = 0; kk < NKK; ++kk) {
             if constexpr (kFp8) ka[kk] = gload8(kb + koff + 32 * kk);
@@ -482,7 +515,7 @@ __global__ __launch_bounds__(64) void decode_stream_kernel(const bf16* __restric
     // The V buffers are distinct arrays, so the compiler does not make LDS
     // reads wait for the other buffer's DMA.
     KReg ka0[NKK], ka1[NKK];
-    issue_page(page_id(cc), cc.kvh, Vb0, ka0);
+    issue_page(page_id(cc), cc, Vb0, ka0);
     Cursor cf = cc;  // page whose loads go out next
     advance(cf);
     int pid_f = cf.x < xe ? page_id(cf) : 0;
@@ -494,7 +527,7 @@ __global__ __launch_bounds__(64) void decode_stream_kernel(const bf16* __restric
         Cursor cn = cf;
         int pid_n = 0;
         if (more) {
-            issue_page(pid_f, cf.kvh, by, ky);
+            issue_page(pid_f, cf, by, ky);
             advance(cn);
             if (cn.x < xe) pid_n = page_id(cn);
             wait_loads<NKK + NDMA>();  // all but the next page's loads
@@ -566,13 +599,21 @@ __device__ __forceinline__ float wave_sum(float x) {
 // parallel/").  The first BATCH partial rows are loaded together with the
 // pieces' lse values, so a run of up to BATCH pieces costs one round trip
 // after the run record.
-template <int D>
+//
+// Append form (kAppend): the wave of each kv group's first head also writes
+// the sequence's newest token (position L - 1) from kn / vn [B, Hkv, d] into
+// its slot of the pools kw / vw.  The split kernel has finished by then, and
+// it read that token from kn / vn, not from the slot.
+template <int D, bool kAppend>
 __global__ __launch_bounds__(64) void decode_combine_kernel(const float* __restrict__ o_part,
                                                             const float* __restrict__ lse_part,
                                                             const int* __restrict__ run_info,
                                                             const int32_t* __restrict__ seq_lens,
                                                             bf16* __restrict__ out, float* __restrict__ lse, int Hq,
-                                                            int Hkv, int G, int pps) {
+                                                            int Hkv, int G, int pps, const bf16* __restrict__ kn,
+                                                            const bf16* __restrict__ vn, bf16* __restrict__ kw,
+                                                            bf16* __restrict__ vw,
+                                                            const int32_t* __restrict__ block_table, int W) {
     constexpr int NDW = D / 64;  // d values per lane
     constexpr int BATCH = 8;
     const int bh = blockIdx.x;
@@ -584,6 +625,19 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(const float* __restr
     const int L = seq_lens[b];
     const int4 info = *reinterpret_cast<const int4*>(run_info + 4 * (size_t)r);
     bf16* orow = out + (size_t)bh * D;
+    if constexpr (kAppend) {
+        constexpr int CPR = D / 8;  // 16-byte chunks per row
+        if (hh == 0 && L > 0 && lane < 2 * CPR) {
+            const int pos = L - 1;
+            const int kvh = h / G;
+            const int c = lane % CPR;
+            const bool isv = lane >= CPR;
+            const size_t page = (size_t)block_table[(size_t)b * W + pos / kPage];
+            const u32x4 val =
+                *reinterpret_cast<const u32x4*>((isv ? vn : kn) + ((size_t)b * Hkv + kvh) * D + 8 * c);
+            *reinterpret_cast<u32x4*>((isv ? vw : kw) + ((page * Hkv + kvh) * kPage + pos % kPage) * D + 8 * c) = val;
+        }
+    }
     if (L == 0) {
 #pragma unroll
         for (int k = 0; k < NDW; ++k) orow[64 * k + lane] = (bf16)0.f;
@@ -650,7 +704,7 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(const float* __restr
 
 // Workgroups of the streaming kernel that are resident at once on `dev`
 // (compute units x occupancy, at most kMaxStreamWaves), found once per device.
-template <int D, bool kFp8>
+template <int D, bool kFp8, bool kAppend>
 hipError_t stream_waves(int dev, int* nw) {
     static std::atomic<int> cache[kMaxDevices];
     if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
@@ -664,7 +718,7 @@ hipError_t stream_waves(int dev, int* nw) {
         int cur = 0;
         if ((e = hipGetDevice(&cur)) != hipSuccess) return e;
         if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, decode_stream_kernel<D, kFp8>, 64, 0);
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, decode_stream_kernel<D, kFp8, kAppend>, 64, 0);
         if (cur != dev) {
             const hipError_t e2 = hipSetDevice(cur);
             if (e == hipSuccess) e = e2;
@@ -678,36 +732,40 @@ hipError_t stream_waves(int dev, int* nw) {
     return hipSuccess;
 }
 
-template <int D, bool kFp8>
-hipError_t launch_split(const DecodeArgs& a, int dev, hipStream_t stream, float c1, float vscale) {
+template <int D, bool kFp8, bool kAppend>
+hipError_t launch_split(const DecodeArgs& a, int dev, hipStream_t stream, float c1, float vscale, const bf16* kn,
+                        const bf16* vn) {
     int nw = 0;
-    const hipError_t e = stream_waves<D, kFp8>(dev, &nw);
+    const hipError_t e = stream_waves<D, kFp8, kAppend>(dev, &nw);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((decode_stream_kernel<D, kFp8>), dim3((unsigned)nw), dim3(64), 0, stream, (const bf16*)a.q,
-                       (const char*)a.k_pages, (const char*)a.v_pages, a.block_table, a.seq_lens, (bf16*)a.out, a.lse,
-                       a.o_part, a.lse_part, a.run_info, a.B, a.Hq, a.Hkv, a.Hq / a.Hkv, a.W, a.pages_per_split, c1,
-                       vscale);
+    hipLaunchKernelGGL((decode_stream_kernel<D, kFp8, kAppend>), dim3((unsigned)nw), dim3(64), 0, stream,
+                       (const bf16*)a.q, (const char*)a.k_pages, (const char*)a.v_pages, a.block_table, a.seq_lens,
+                       (bf16*)a.out, a.lse, a.o_part, a.lse_part, a.run_info, a.B, a.Hq, a.Hkv, a.Hq / a.Hkv, a.W,
+                       a.pages_per_split, c1, vscale, kn, vn);
     return hipGetLastError();
 }
 
-template <bool kFp8>
-hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream, float kscale, float vscale) {
+template <int D, bool kAppend>
+hipError_t launch_combine(const DecodeArgs& a, hipStream_t stream, const bf16* kn, const bf16* vn) {
+    hipLaunchKernelGGL((decode_combine_kernel<D, kAppend>), dim3((unsigned)a.B * a.Hq), dim3(64), 0, stream, a.o_part,
+                       a.lse_part, a.run_info, a.seq_lens, (bf16*)a.out, a.lse, a.Hq, a.Hkv, a.Hq / a.Hkv,
+                       a.pages_per_split, kn, vn, (bf16*)a.k_pages, (bf16*)a.v_pages, a.block_table, a.W);
+    return hipGetLastError();
+}
+
+// kn / vn: the newest token's key and value rows [B, Hkv, d] (append form),
+// or null.
+template <bool kFp8, bool kAppend>
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream, float kscale, float vscale,
+                         const bf16* kn = nullptr, const bf16* vn = nullptr) {
     const float c1 = (float)((double)a.scale * (double)kscale * 1.4426950408889634);
     hipDevice_t dev = 0;
     hipError_t e = hipStreamGetDevice(stream, &dev);
     if (e != hipSuccess) return e;
-    e = a.d == 128 ? launch_split<128, kFp8>(a, dev, stream, c1, vscale)
-                   : launch_split<64, kFp8>(a, dev, stream, c1, vscale);
+    e = a.d == 128 ? launch_split<128, kFp8, kAppend>(a, dev, stream, c1, vscale, kn, vn)
+                   : launch_split<64, kFp8, kAppend>(a, dev, stream, c1, vscale, kn, vn);
     if (e != hipSuccess) return e;
-    const int G = a.Hq / a.Hkv;
-    if (a.d == 128) {
-        hipLaunchKernelGGL(decode_combine_kernel<128>, dim3((unsigned)a.B * a.Hq), dim3(64), 0, stream, a.o_part,
-                           a.lse_part, a.run_info, a.seq_lens, (bf16*)a.out, a.lse, a.Hq, a.Hkv, G, a.pages_per_split);
-    } else {
-        hipLaunchKernelGGL(decode_combine_kernel<64>, dim3((unsigned)a.B * a.Hq), dim3(64), 0, stream, a.o_part,
-                           a.lse_part, a.run_info, a.seq_lens, (bf16*)a.out, a.lse, a.Hq, a.Hkv, G, a.pages_per_split);
-    }
-    return hipGetLastError();
+    return a.d == 128 ? launch_combine<128, kAppend>(a, stream, kn, vn) : launch_combine<64, kAppend>(a, stream, kn, vn);
 }
 
 // Workspace of attn_decode_paged_noalloc, for callers that cannot allocate:
@@ -747,11 +805,16 @@ hipError_t decode_scratch(hipStream_t stream, void** ptr) {
 }
 
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream) {
-    return launch_decode<false>(a, stream, 1.0f, 1.0f);
+    return launch_decode<false, false>(a, stream, 1.0f, 1.0f);
+}
+
+hipError_t launch_decode_append_bf16(const DecodeArgs& a, const void* k_new, const void* v_new, hipStream_t stream) {
+    return launch_decode<false, true>(a, stream, 1.0f, 1.0f, static_cast<const bf16*>(k_new),
+                                      static_cast<const bf16*>(v_new));
 }
 
 hipError_t launch_decode_fp8(const DecodeArgs& a, float kscale, float vscale, hipStream_t stream) {
-    return launch_decode<true>(a, stream, kscale, vscale);
+    return launch_decode<true, false>(a, stream, kscale, vscale);
 }
 
 }  // namespace attn

@@ -73,6 +73,10 @@ inline int64_t varlen_items_bound(int64_t N, int64_t S, int64_t Tmax, int64_t BM
     return a < b ? a : b;
 }
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream);
+// The same decode with the newest token of each sequence (position
+// seq_lens[b] - 1) given as k_new / v_new [B, Hkv, d] rather than in the
+// pools; the launch also writes it into its slot of a.k_pages / a.v_pages.
+hipError_t launch_decode_append_bf16(const DecodeArgs& a, const void* k_new, const void* v_new, hipStream_t stream);
 // FP8 E4M3 page pools (one byte per value) with per-tensor scales.
 hipError_t launch_decode_fp8(const DecodeArgs& a, float kscale, float vscale, hipStream_t stream);
 hipError_t launch_kv_append_bf16(const KvAppendArgs& a, hipStream_t stream);

@@ -134,6 +134,9 @@ WORKLOADS[7] = {"append": ChunkShape(4, 32, 8, 2048, 128, PAGE_SIZE, 4096, 16384
 # arriving as dense tensors instead of already cached.
 WORKLOADS[11] = {"fused": ChunkShape(4, 32, 8, 2048, 128, PAGE_SIZE, 4096, 16384, torch.bfloat16)}
 
+# Paged decode with the newest token's KV append fused (seed 112): workload 4's decode shape.
+WORKLOADS[12] = {"decode_append": DecodeShape(32, 16, 8, 128, PAGE_SIZE, 32, 2048, torch.bfloat16)}
+
 # Ragged prefill (seed 8): 16 sequences of 256..4096 tokens packed along the token axis.
 WORKLOADS[8] = {"varlen": VarlenShape(16, 32, 8, 128, 256, 4096, torch.bfloat16)}
 
@@ -155,6 +158,7 @@ WORKLOAD_NAMES = {
     9: "paged decode over an FP8 E4M3 cache B64 Hq32 Hkv8 d128 page16 L~U[1024,8192]",
     10: "paged decode bf16 serving batch B1024 Hq32 Hkv8 d128 page16 L~U[16,512]",
     11: "KV append + chunked prefill bf16 in one launch B4 Hq32 Hkv8 Tq2048 d128 page16 L~U[4096,16384]",
+    12: "paged decode bf16 with the newest token's KV append fused B32 Hq16 Hkv8 d128 page16 L~U[32,2048]",
 }
 
 
@@ -348,6 +352,25 @@ def fused_inputs(shape: ChunkShape, seed: int, *, seq_lens=None, poison=None, st
         a.k_pages[pages, :, slots] = stale
         a.v_pages[pages, :, slots] = stale
     return FusedInputs(q, a.k_new, a.v_new, a.k_pages, a.v_pages, a.block_table, a.seq_lens, a.page_size)
+
+
+def decode_append_inputs(shape: DecodeShape, seed: int, *, seq_lens=None, poison=None, stale=None):
+    """Inputs of the decode with the newest token's append fused: paged_inputs(shape, seed, ...) (seq_lens
+    are the lengths after the append), then k_new, v_new [B, Hkv, d] from a generator seeded seed + 1000000.
+    ``stale``, if given, fills each sequence's newest-token slot in the pools (values the call overwrites and
+    must never read).  Returns (PagedInputs, k_new, v_new)."""
+    inp = paged_inputs(shape, seed, seq_lens=seq_lens, poison=poison)
+    B = inp.q.shape[0]
+    g = torch.Generator().manual_seed(seed + 1000000)
+    k_new = torch.randn(B, shape.Hkv, shape.d, generator=g).to(shape.dtype)
+    v_new = torch.randn(B, shape.Hkv, shape.d, generator=g).to(shape.dtype)
+    if stale is not None:
+        for b, L in enumerate(inp.seq_lens.tolist()):
+            if L > 0:
+                page = int(inp.block_table[b, (L - 1) // shape.page_size])
+                inp.k_pages[page, :, (L - 1) % shape.page_size] = stale
+                inp.v_pages[page, :, (L - 1) % shape.page_size] = stale
+    return inp, k_new, v_new
 
 
 @dataclass

@@ -31,7 +31,7 @@ its clock), except where the host issues a step more slowly than the GPU
 runs it.  ``environment`` names the GPU, ROCm and torch, and the GFX clock
 amdsmi reports while the dominant kernel runs.
 
-    python bench.py [--steps K] [--warmup W] [--workload 5|3|4|6|7|8|9|10|11] [--no-cpu-baseline] [--flush]
+    python bench.py [--steps K] [--warmup W] [--workload 5|3|4|6|7|8|9|10|11|12] [--no-cpu-baseline] [--flush]
 
 ``--flush`` reads a 512 MiB buffer before every step (outside the events),
 so that a decode whose K/V would fit in the 256 MB MALL (workload 4) starts
@@ -42,6 +42,8 @@ Workload 6 (not the default) times the chunked prefill over a paged cache:
 Workload 7 times the KV append that writes such chunks into the cache, and
 workload 11 the two in one launch (the chunk's keys and values arriving as
 dense tensors, read from there and written into the cache by the prefill).
+Workload 12 times workload 4's decode with each sequence's newest token
+appended by the same two launches.
 Workload 8 times the ragged prefill of 16 sequences of 256..4096 tokens
 packed along the token axis.  Workload 9 times the paged decode of workload
 5 over an FP8 E4M3 cache (algorithmic bytes: one byte per cached value).
@@ -171,7 +173,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workload", type=int, default=5, choices=(3, 4, 5, 6, 7, 8, 9, 10, 11))
+    p.add_argument("--workload", type=int, default=5, choices=(3, 4, 5, 6, 7, 8, 9, 10, 11, 12))
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--sequential", action="store_true",
                    help="run the parts of a two-part step (workload 5) one after the other on one stream; by default "
@@ -455,6 +457,34 @@ def cpu_baseline_varlen(var_in, shape, budget_s=20.0):
             "varlen_tflops": flops / t / 1e12, "host_cpu_count": os.cpu_count()}
 
 
+def cpu_baseline_decode_append(inp, kn, vn, budget_s=20.0):
+    """Time the fp64 oracle's decode with the fused append on a bounded sample: sequences one at a time."""
+    import oracle
+    from threadpoolctl import threadpool_info
+
+    threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    kp, vp = inp.k_pages.float().numpy(), inp.v_pages.float().numpy()
+    kn, vn = kn.float().numpy(), vn.float().numpy()
+    scale = synth.fp32_scale(inp.q.shape[2])
+    B, Hq, d = inp.q.shape
+    Hkv = kp.shape[1]
+    t0 = time.perf_counter()
+    seqs = nbytes = 0
+    while seqs < B and (seqs == 0 or time.perf_counter() - t0 < budget_s):
+        b = seqs
+        oracle.decode_paged_append(inp.q[b:b + 1].float().numpy(), kn[b:b + 1], vn[b:b + 1], kp, vp,
+                                   inp.block_table[b:b + 1].numpy(), inp.seq_lens[b:b + 1].numpy(), scale,
+                                   inp.page_size)
+        L = int(inp.seq_lens[b])
+        nbytes += 2 * L * Hkv * d * 2 + 2 * Hq * d * 2 + 4 * (-(-L // 16)) + 4 + 2 * Hkv * d * 2
+        seqs += 1
+    t = time.perf_counter() - t0
+    return {"value": nbytes / t / PEAK_HBM_BYTES, "unit": "fraction of MI355X roofline", "cores": threads,
+            "kind": "oracle", "sample": f"fp64 oracle decode with the append of {seqs} of {B} sequences ({t:.2f} s, "
+                                        f"each call copying both pools)",
+            "decode_gbps": nbytes / t / 1e9, "host_cpu_count": os.cpu_count()}
+
+
 def cpu_baseline_fp8(inp, budget_s=20.0):
     """Time the fp64 oracle's FP8 decode on a bounded sample: sequences one at a time."""
     import oracle
@@ -503,8 +533,9 @@ def main():
     var_shape = wl.get("varlen")
     f8_shape = wl.get("decode_fp8")
     fu_shape = wl.get("fused")
+    da_shape = wl.get("decode_append")
 
-    pre_inputs = dec_inputs = chunk_in = app_in = var_in = f8_in = fu_in = None
+    pre_inputs = dec_inputs = chunk_in = app_in = var_in = f8_in = fu_in = da_in = None
     work = {}
     if pre_shape is not None:
         pre_inputs = synth.prefill_inputs(pre_shape, seed=args.workload)
@@ -551,6 +582,20 @@ def main():
         uscale = synth.fp32_scale(fu_shape.d)
         work["fused"] = lambda: A.attn_prefill_paged_append(uq, ukn, uvn, ukp, uvp, ubt, usl, out=uout, lse=ulse,
                                                             scale=uscale)
+    if da_shape is not None:
+        # Every step writes the same newest tokens into the same slots, and
+        # the decode reads them from k_new / v_new: steps repeat exactly.
+        da_in, da_kn, da_vn = synth.decode_append_inputs(da_shape, seed=100 + args.workload)
+        eq, ekp, evp, ebt, esl, ekn, evn = (t.to(dev) for t in (da_in.q, da_in.k_pages, da_in.v_pages,
+                                                                da_in.block_table, da_in.seq_lens, da_kn, da_vn))
+        eout = torch.empty_like(eq)
+        else_ = torch.empty(eq.shape[0], eq.shape[1], dtype=torch.float32, device=dev)
+        eneed = A.attn_decode_workspace_bytes(da_shape.B, da_shape.Hq, da_shape.Hkv, da_shape.d, da_shape.page_size,
+                                              da_in.max_pages_per_seq, 0)
+        ews = torch.empty(eneed, dtype=torch.uint8, device=dev)
+        escale = synth.fp32_scale(da_shape.d)
+        work["decode_append"] = lambda: A.attn_decode_paged_append(eq, ekn, evn, ekp, evp, ebt, esl, out=eout,
+                                                                   lse=else_, scale=escale, workspace=ews)
     if var_shape is not None:
         var_in = synth.varlen_inputs(var_shape, seed=args.workload)
         vq, vk, vv, vcu = (t.to(dev) for t in var_in[:4])
@@ -797,6 +842,16 @@ def main():
         parts["chunk"] = {"ms": round(ms["chunk"], 4), **spread("chunk"),
                           "tflops": round(flops / t / 1e12, 1), "frac_of_peak": round(flops / t / PEAK_BF16_FLOPS, 4),
                           "flops_per_launch": flops}
+    if da_shape is not None:
+        # the decode's bytes (the newest token's K/V counted once, read from
+        # k_new / v_new) plus the append's write of that token into the pools
+        nbytes = da_in.algorithmic_bytes() + 2 * da_kn.numel() * da_kn.element_size()
+        t = ms["decode_append"] / 1e3
+        at_peak += nbytes / PEAK_HBM_BYTES
+        parts["decode_append"] = {"ms": round(ms["decode_append"], 4), **spread("decode_append"),
+                                  "gbps": round(nbytes / t / 1e9, 1),
+                                  "frac_of_peak": round(nbytes / t / PEAK_HBM_BYTES, 4), "bytes_per_launch": nbytes,
+                                  "kernels": "stream + combine (append forms)"}
     if fu_shape is not None:
         flops = synth.chunk_flops(fu_shape.Hq, fu_shape.d, fu_shape.Tq, fu_in.seq_lens.tolist())
         t = ms["fused"] / 1e3
@@ -852,6 +907,13 @@ def main():
                 "frac": round(parts["decode_fp8"]["gbps"] * 1e9 / PEAK_HBM_BYTES, 4),
                 "traffic": measured_traffic(args.workload, "decode_stream_kernel+decode_combine_kernel", src),
                 "source_hash": src}
+    elif dom == "decode_append":
+        src = kernel_source_hash(["decode_paged.hip", "device_common.h"])
+        roof = {"kernel": "decode_stream_kernel+decode_combine_kernel (append form)", "bound": "hbm",
+                "achieved": parts[dom]["gbps"], "peak": PEAK_HBM_BYTES / 1e9, "unit": "GB/s",
+                "frac": round(parts[dom]["gbps"] * 1e9 / PEAK_HBM_BYTES, 4),
+                "traffic": measured_traffic(args.workload, "decode_stream_kernel+decode_combine_kernel", src),
+                "source_hash": src}
     elif dom == "append":
         src = kernel_source_hash(["kv_append.hip", "device_common.h"])
         roof = {"kernel": "kv_append_kernel", "bound": "hbm", "achieved": parts["append"]["gbps"],
@@ -895,6 +957,9 @@ def main():
     if chunk_in is not None:
         cfg["seed_chunk"] = args.workload
         cfg["chunk_seq_lens"] = chunk_in.seq_lens.tolist()
+    if da_in is not None:
+        cfg["seed_decode"] = 100 + args.workload
+        cfg["decode_tokens"] = int(da_in.seq_lens.sum())
     if fu_in is not None:
         cfg["seed_fused"] = args.workload
         cfg["fused_seq_lens"] = fu_in.seq_lens.tolist()
@@ -932,6 +997,8 @@ def main():
         result["cpu_baseline"] = cpu_baseline_chunk(chunk_in)
     if not args.no_cpu_baseline and args.workload == 7:
         result["cpu_baseline"] = cpu_baseline_append(app_in)
+    if not args.no_cpu_baseline and args.workload == 12:
+        result["cpu_baseline"] = cpu_baseline_decode_append(da_in, da_kn, da_vn)
     if not args.no_cpu_baseline and args.workload == 11:
         result["cpu_baseline"] = cpu_baseline_fused(fu_in)
     if not args.no_cpu_baseline and args.workload == 9:

@@ -1,7 +1,7 @@
 /*
  * attn.h — causal multi-head / grouped-query attention for MI355X (gfx950).
  *
- * Seven operations, all hand-written HIP kernels behind a plain C ABI:
+ * Eight operations, all hand-written HIP kernels behind a plain C ABI:
  *
  *  - attn_prefill: causal self-attention of T queries over the same T keys,
  *    computed block by block with an online softmax so that the T x T score
@@ -45,6 +45,11 @@
  *    them from there (and the older keys from the pages), and the same
  *    launch writes them into their page slots.  Same results as
  *    attn_kv_append followed by attn_prefill_paged, bit for bit.
+ *
+ *  - attn_decode_paged_append: the one-token KV append fused into the paged
+ *    decode (the newest token read from dense tensors, written into its
+ *    slot by the combine kernel); bit for bit attn_kv_append followed by
+ *    attn_decode_paged.
  *
  * What is computed.  For query head h, the kv head read is h / (Hq / Hkv)
  * (consecutive groups of query heads share one kv head).  For a query q and
@@ -291,6 +296,35 @@ int attn_decode_paged(const void* q, const void* k_pages, const void* v_pages,
                       int max_pages_per_seq, float scale, int dtype,
                       int num_splits, void* workspace, size_t workspace_bytes,
                       hipStream_t stream);
+
+/*
+ * Decode with the KV append fused: the work of attn_kv_append with Tn = 1
+ * (k_new, v_new written at position seq_lens[b] - 1) followed by
+ * attn_decode_paged, in the same two launches as the decode alone; out, lse
+ * and the pools come out bit for bit as from those two calls (same
+ * num_splits).  The split kernel reads the newest token from k_new / v_new,
+ * not from its slot; the combine kernel, which runs after it, writes the
+ * slot.
+ *
+ *   k_new, v_new   : device, [B, Hkv, d] (the layout of [B, Hkv, 1, d]): the
+ *                    newest token's key and value per sequence and kv head
+ *   k_pages,v_pages: as for attn_decode_paged; written only at the slot of
+ *                    position seq_lens[b] - 1 of each sequence
+ *   seq_lens       : lengths after the append; a sequence with 0 appends
+ *                    nothing and decodes to out = 0, lse = -inf
+ *   other arguments: as for attn_decode_paged (dtype ATTN_BF16 only)
+ * Two sequences' newest tokens must not name the same (page, slot), and no
+ * sequence may read another's newest-token slot as part of its cache.
+ * Calls that share a workspace must not overlap in time.
+ */
+int attn_decode_paged_append(const void* q, const void* k_new, const void* v_new,
+                             void* k_pages, void* v_pages,
+                             const int32_t* block_table, const int32_t* seq_lens,
+                             void* out, float* lse,
+                             int B, int Hq, int Hkv, int d, int page_size, int num_pages,
+                             int max_pages_per_seq, float scale, int dtype,
+                             int num_splits, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream);
 
 /*
  * attn_decode_paged without a workspace argument, for callers that cannot

@@ -23,6 +23,7 @@ source and checks that the pins catch each one.
 
 from .attention import (  # noqa: F401
     decode_paged,
+    decode_paged_append,
     decode_paged_fp8,
     fp8_e4m3_value,
     gather_pages,

@@ -271,6 +271,28 @@ def prefill_paged_append(q, k_new, v_new, k_pages, v_pages, block_table, seq_len
     return out, lse, k_after, v_after
 
 
+def decode_paged_append(q, k_new, v_new, k_pages, v_pages, block_table, seq_lens, scale, page_size):
+    """KV append of each sequence's newest token followed by the paged decode.
+
+    The decode step of a paged-cache server (RoseLLM README, "Systems
+    highlights", "Inference and serving": the KV-cache writer, then decode
+    over the paged cache): k_new / v_new [B, Hkv, d] (or [B, Hkv, 1, d]) are
+    written at position seq_lens[b] - 1 (kv_append with one token), then the
+    query of each sequence attends over its seq_lens[b] cached tokens
+    (decode_paged).  A sequence with seq_lens[b] = 0 appends nothing.
+    Returns (out, lse, k_pages after, v_pages after).
+    """
+    B = np.shape(q)[0]
+    kn = np.asarray(k_new).reshape(B, -1, 1, np.shape(k_new)[-1])
+    vn = np.asarray(v_new).reshape(B, -1, 1, np.shape(v_new)[-1])
+    sl = np.asarray(seq_lens)
+    some = np.nonzero(sl > 0)[0]
+    k_after, v_after = kv_append(k_pages, v_pages, kn[some], vn[some], np.asarray(block_table)[some], sl[some],
+                                 page_size)
+    out, lse = decode_paged(q, k_after, v_after, block_table, seq_lens, scale, page_size)
+    return out, lse, k_after, v_after
+
+
 def prefill_varlen(q, k, v, cu_seqlens, scale):
     """Causal prefill of a ragged batch packed along the token axis.
 

@@ -27,7 +27,8 @@ def declared_functions():
 
 def test_header_declares_the_api():
     names = declared_functions()
-    for n in ("attn_prefill", "attn_prefill_paged", "attn_prefill_paged_append", "attn_prefill_varlen",
+    for n in ("attn_prefill", "attn_prefill_paged", "attn_prefill_paged_append", "attn_decode_paged_append",
+              "attn_prefill_varlen",
               "attn_validate_varlen_metadata",
               "attn_kv_append", "attn_decode_paged_fp8", "attn_decode_paged", "attn_decode_workspace_bytes",
               "attn_decode_num_splits", "attn_validate_paged_metadata", "attn_validate_chunk_metadata",
@@ -117,6 +118,47 @@ def decode(lib, q=FAKE, kp=FAKE, vp=FAKE, bt=FAKE, sl=FAKE, out=FAKE, lse=None, 
 )
 def test_decode_rejects(lib, kw, status):
     assert decode(lib, **kw) == status
+
+
+def decode_append(lib, q=FAKE, kn=FAKE, vn=FAKE, kp=FAKE, vp=FAKE, bt=FAKE, sl=FAKE, out=FAKE, lse=None, B=2, Hq=4,
+                  Hkv=2, d=128, ps=16, P=10, W=8, scale=0.1, dtype=1, ns=0, ws=FAKE, wsb=None):
+    if wsb is None:
+        wsb = lib.attn_decode_workspace_bytes(max(B, 0), Hq, Hkv, d, ps, W, ns) if B >= 0 else 0
+    return lib.attn_decode_paged_append(q, kn, vn, kp, vp, bt, sl, out, lse, B, Hq, Hkv, d, ps, P, W, scale, dtype,
+                                        ns, ws, wsb, None)
+
+
+@pytest.mark.parametrize(
+    "kw,status",
+    [
+        (dict(q=None), A.ATTN_ERR_INVALID_ARG),
+        (dict(kn=None), A.ATTN_ERR_INVALID_ARG),
+        (dict(vn=None), A.ATTN_ERR_INVALID_ARG),
+        (dict(vp=None), A.ATTN_ERR_INVALID_ARG),
+        (dict(sl=None), A.ATTN_ERR_INVALID_ARG),
+        (dict(kn=FAKE + 8), A.ATTN_ERR_INVALID_ARG),
+        (dict(vn=FAKE + 2), A.ATTN_ERR_INVALID_ARG),
+        (dict(bt=FAKE + 2), A.ATTN_ERR_INVALID_ARG),
+        (dict(Hq=5, Hkv=2), A.ATTN_ERR_INVALID_ARG),
+        (dict(B=-1), A.ATTN_ERR_INVALID_ARG),
+        (dict(W=0), A.ATTN_ERR_INVALID_ARG),
+        (dict(ns=-2), A.ATTN_ERR_INVALID_ARG),
+        (dict(scale=float("inf")), A.ATTN_ERR_INVALID_ARG),
+        (dict(dtype=0), A.ATTN_ERR_UNSUPPORTED),
+        (dict(d=80), A.ATTN_ERR_UNSUPPORTED),
+        (dict(ps=32), A.ATTN_ERR_UNSUPPORTED),
+        (dict(ws=None), A.ATTN_ERR_WORKSPACE),
+        (dict(wsb=16), A.ATTN_ERR_WORKSPACE),
+    ],
+)
+def test_decode_append_rejects(lib, kw, status):
+    assert decode_append(lib, **kw) == status
+    assert A.attn_last_error_message() != ""
+
+
+def test_decode_append_empty_batch_is_a_no_op(lib):
+    assert decode_append(lib, q=None, kn=None, vn=None, kp=None, vp=None, bt=None, sl=None, out=None, B=0, ws=None,
+                         wsb=0) == A.ATTN_OK
 
 
 def decode_noalloc(lib, q=FAKE, kp=FAKE, vp=FAKE, bt=FAKE, sl=FAKE, out=FAKE, lse=None, B=2, Hq=4, Hkv=2, d=128,

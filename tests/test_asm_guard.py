@@ -143,3 +143,16 @@ def test_a_uniform_copy_made_on_two_paths_keeps_its_value_through_joins_and_the_
     # between the two comparisons is caught as before
     assert hazards(asm.replace("\ts_cbranch_vccz .LBB0_6\n; %bb.5:", "\tv_mov_b64_e32 v[4:5], s[16:17]\n"
                                "\ts_cbranch_vccz .LBB0_6\n; %bb.5:")) == ["k: v_mov_b32_e32 v1, v50"]
+
+
+def test_an_execz_branch_under_the_whole_wave_mask_is_not_taken():
+    # the structurizer's "skip the arm if no lane is left in it" test: under
+    # the whole wave's mask the skip cannot happen, so the wait in the arm
+    # always runs before the write
+    tail = ("\ts_cbranch_execz .LBB0_2\n; %bb.1:\n\ts_waitcnt vmcnt(0)\n"
+            ".LBB0_2:\n\ts_or_b64 exec, exec, s[0:1]\n\tv_mov_b32_e32 v51, 0\n\ts_endpgm\n")
+    assert hazards(k(LOAD + "\ts_mov_b64 s[0:1], 0\n" + tail)) == []
+    # under a mask that may be empty (s_and_saveexec of a lane condition) the
+    # arm, and its wait, may be skipped: the write is reported
+    masked = LOAD + "\tv_cmp_gt_u32_e32 vcc, 4, v0\n\ts_and_saveexec_b64 s[0:1], vcc\n" + tail
+    assert hazards(k(masked)) == ["k: v_mov_b32_e32 v51, 0"]

@@ -57,6 +57,6 @@ def test_committed_traffic_lines_are_well_formed(bench):
     assert lines, "no traffic lines in the committed counter summary"
     for parts in lines:
         assert len(parts) == 5
-        assert int(parts[1]) in (3, 4, 5, 6, 7, 8, 9, 10, 11)
+        assert int(parts[1]) in (3, 4, 5, 6, 7, 8, 9, 10, 11, 12)
         assert len(parts[3]) == 16 and int(parts[3], 16) >= 0
         assert int(parts[4]) > 0

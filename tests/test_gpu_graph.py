@@ -83,3 +83,45 @@ def test_fused_append_graph_replays_rewrite_the_cache():
             assert torch.equal(got.view(torch.int16) if got.dtype == torch.bfloat16 else got,
                                want.view(torch.int16) if want.dtype == torch.bfloat16 else want), \
                 f"replay {r}: {name} differs from the eager launch"
+
+
+def test_decode_append_graph_replays_rewrite_the_cache():
+    """The decode with the fused append under capture: before every replay the newest tokens' slots are set
+    back to NaN and the outputs cleared; every replay must write the same slots and outputs as the eager call."""
+    dev = device()
+    shp = synth.DecodeShape(6, 8, 2, 128, 16, 1, 900, torch.bfloat16)
+    inp, kn, vn = synth.decode_append_inputs(shp, seed=24, poison=float("nan"), stale=float("nan"))
+    q, kp, vp, bt, sl = (t.to(dev) for t in (inp.q, inp.k_pages, inp.v_pages, inp.block_table, inp.seq_lens))
+    kn, vn = kn.to(dev), vn.to(dev)
+    out = torch.empty_like(q)
+    lse = torch.empty(6, 8, dtype=torch.float32, device=dev)
+    ws = torch.empty(A.attn_decode_workspace_bytes(6, 8, 2, 128, 16, inp.max_pages_per_seq, 0), dtype=torch.uint8,
+                     device=dev)
+    L = inp.seq_lens.long()
+    pages = inp.block_table.long()[torch.arange(6), (L - 1) // 16].to(dev)
+    slots = ((L - 1) % 16).to(dev)
+    scale = synth.fp32_scale(128)
+
+    def work():
+        A.attn_decode_paged_append(q, kn, vn, kp, vp, bt, sl, out=out, lse=lse, scale=scale, workspace=ws)
+
+    say("[graph] decode append: eager reference")
+    work()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (out, lse, kp, vp)]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        work()
+    for r in range(4):
+        say(f"[graph] decode append: replay {r}")
+        out.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        kp[pages, :, slots] = float("nan")
+        vp[pages, :, slots] = float("nan")
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for name, got, want in zip(("out", "lse", "k_pages", "v_pages"), (out, lse, kp, vp), ref):
+            assert torch.equal(got.view(torch.int16) if got.dtype == torch.bfloat16 else got,
+                               want.view(torch.int16) if want.dtype == torch.bfloat16 else want), \
+                f"replay {r}: {name} differs from the eager launch"

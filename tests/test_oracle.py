@@ -443,6 +443,39 @@ def test_fused_chunks_rebuild_a_dense_prefill():
             np.testing.assert_array_equal(oracle.gather_pages(vp, table[b], L, ps, kvh), v[b, kvh])
 
 
+def test_fused_decode_steps_rebuild_a_dense_prefill():
+    """Decode two sequences token by token through the fused append + decode, from an empty (NaN) cache,
+    the second starting three steps later (seq_lens 0 meanwhile: nothing appended, out 0, lse -inf): every
+    step's output is the matching row of a dense causal prefill, and the final cache holds every token."""
+    r = rng(44)
+    B, Hq, Hkv, d, ps, T, lag = 2, 4, 2, 3, 4, 9, 3
+    q = 2.0 * r.standard_normal((B, Hq, T, d))
+    k = r.standard_normal((B, Hkv, T, d))
+    v = r.standard_normal((B, Hkv, T, d))
+    W = -(-T // ps)
+    table = r.permutation(B * W).reshape(B, W)
+    kp = np.full((B * W, Hkv, ps, d), np.nan)
+    vp = np.full((B * W, Hkv, ps, d), np.nan)
+    od, ld = oracle.prefill(q, k, v, 0.8)
+    for t in range(T):
+        L = np.array([t + 1, max(0, t + 1 - lag)])
+        pos = np.maximum(L - 1, 0)
+        qs = np.stack([q[b, :, pos[b]] for b in range(B)])
+        kn = np.stack([k[b, :, pos[b]] if L[b] else np.full((Hkv, d), np.nan) for b in range(B)])
+        vn = np.stack([v[b, :, pos[b]] if L[b] else np.full((Hkv, d), np.nan) for b in range(B)])
+        out, lse, kp, vp = oracle.decode_paged_append(qs, kn, vn, kp, vp, table, L, 0.8, ps)
+        for b in range(B):
+            if L[b]:
+                np.testing.assert_allclose(out[b], od[b, :, pos[b]], rtol=0, atol=1e-13)
+                np.testing.assert_allclose(lse[b], ld[b, :, pos[b]], rtol=0, atol=1e-13)
+            else:
+                assert np.all(out[b] == 0) and np.all(lse[b] == -np.inf)
+    for b, Lb in enumerate((T, T - lag)):
+        for kvh in range(Hkv):
+            np.testing.assert_array_equal(oracle.gather_pages(kp, table[b], Lb, ps, kvh), k[b, kvh, :Lb])
+            np.testing.assert_array_equal(oracle.gather_pages(vp, table[b], Lb, ps, kvh), v[b, kvh, :Lb])
+
+
 # ---------------------------------------------------------------- ragged (varlen) prefill
 def varlen_case(seed, lens, Hq=4, Hkv=2, d=3):
     r = rng(seed)

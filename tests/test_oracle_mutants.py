@@ -79,7 +79,20 @@ MUTATIONS = {
          "page_size, rows=rows)\n    k_after, v_after = kv_append(k_pages, v_pages, k_new, v_new, block_table, "
          "seq_lens, page_size)\n    return out, lse, k_after, v_after"),
     ],
-    "fused step returns the old cache": [("    return out, lse, k_after, v_after", "    return out, lse, k_pages, v_pages")],
+    "fused step returns the old cache": [("rows=rows)\n    return out, lse, k_after, v_after",
+                                          "rows=rows)\n    return out, lse, k_pages, v_pages")],
+    "fused decode returns the old cache": [("scale, page_size)\n    return out, lse, k_after, v_after",
+                                            "scale, page_size)\n    return out, lse, k_pages, v_pages")],
+    "fused decode attends before appending": [
+        ("    out, lse = decode_paged(q, k_after, v_after, block_table, seq_lens, scale, page_size)",
+         "    out, lse = decode_paged(q, k_pages, v_pages, block_table, seq_lens, scale, page_size)"),
+    ],
+    "fused decode appends the new token one slot late": [
+        ("    some = np.nonzero(sl > 0)[0]\n    k_after, v_after = kv_append(k_pages, v_pages, kn[some], vn[some], "
+         "np.asarray(block_table)[some], sl[some],",
+         "    some = np.nonzero(sl > 0)[0]\n    k_after, v_after = kv_append(k_pages, v_pages, kn[some], vn[some], "
+         "np.asarray(block_table)[some], sl[some] + 1,"),
+    ],
     "append writes V into K": [("k_out[page, :, position % page_size] = np.asarray(k_new)[b, :, t]",
                                 "k_out[page, :, position % page_size] = np.asarray(v_new)[b, :, t]")],
 }
