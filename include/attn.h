@@ -40,15 +40,18 @@
  *    "Systems highlights", "Inference and serving"), the step before decode
  *    or chunked prefill reads them.
  *
- *  - attn_prefill_paged_append: KV append and chunked prefill in one launch:
- *    the chunk's keys and values arrive as dense tensors, the attention reads
- *    them from there (and the older keys from the pages), and the same
- *    launch writes them into their page slots.  Same results as
- *    attn_kv_append followed by attn_prefill_paged, bit for bit.
+ *  - attn_prefill_paged_append: KV append and chunked prefill in one launch
+ *    (the fused KV append of the RoseLLM README, "Systems highlights",
+ *    "Inference and serving", with its chunked prefill): the chunk's keys
+ *    and values arrive as dense tensors, the attention reads them from there
+ *    (and the older keys from the pages), and the same launch writes them
+ *    into their page slots.  Same results as attn_kv_append followed by
+ *    attn_prefill_paged, bit for bit.
  *
  *  - attn_decode_paged_append: the one-token KV append fused into the paged
- *    decode (the newest token read from dense tensors, written into its
- *    slot by the combine kernel); bit for bit attn_kv_append followed by
+ *    decode (the same README passage, with its paged decode): the newest
+ *    token is read from dense tensors and written into its slot by the
+ *    combine kernel; bit for bit attn_kv_append followed by
  *    attn_decode_paged.
  *
  * What is computed.  For query head h, the kv head read is h / (Hq / Hkv)
