@@ -52,6 +52,12 @@ design notes of the repository):
   visible key: the sum is empty, so lse = ln 0 = -inf, and out is defined
   as 0.
 
+  Fused KV append (RoseLLM README, "Systems highlights", "Inference and
+  serving"): the append of a chunk's keys and values (or of each sequence's
+  newest token) composed with the chunked prefill (or the decode) that
+  follows it, the two steps in that order: prefill_paged_append,
+  decode_paged_append.
+
 Arithmetic is NumPy float64 throughout.  Inputs may be any real dtype; bf16
 tensors must be converted by the caller (exactly, via float32) before they
 arrive here.
